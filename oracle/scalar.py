@@ -1,0 +1,99 @@
+"""Pure-Python scalar brute force for tiny shapes (oracle; test
+infrastructure only).
+
+A second, independent route to the same definitions as ``quant`` and
+``attention``: no NumPy, no frexp and no sorted-table search.  The shared
+exponent is found by stepping a power of two, each element is rounded by
+scanning every code of the format, and attention is written as explicit loops
+with math.exp / math.fsum.  Used only to cross-check the vectorised oracle on
+inputs small enough for loops.
+"""
+
+import math
+import struct
+
+_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def bf16_value(bits):
+    return struct.unpack("<f", struct.pack("<I", (bits & 0xFFFF) << 16))[0]
+
+
+def e4m3_value(code):
+    if code & 0x7F == 0x7F:
+        return math.nan
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 0:
+        return s * m * 2.0 ** -9
+    return s * (8 + m) * 2.0 ** (e - 10)
+
+
+def e2m1_value(code):
+    return (-1.0 if code & 8 else 1.0) * _E2M1[code & 7]
+
+
+def floor_log2(a):
+    """Largest integer e with 2**e <= a (a > 0), by stepping."""
+    e = 0
+    while 2.0 ** e > a:
+        e -= 1
+    while 2.0 ** (e + 1) <= a:
+        e += 1
+    return e
+
+
+def nearest_code(y, codes, value_of):
+    """Code whose value is nearest to y; ties go to the code with an even
+    mantissa LSB (even code).  Only codes with the sign of y are scanned, so a
+    negative y that rounds to zero keeps its sign bit."""
+    neg = math.copysign(1.0, y) < 0
+    best = None
+    for c in codes:
+        v = value_of(c)
+        if math.isnan(v) or (math.copysign(1.0, v) < 0) != neg:
+            continue
+        dist = abs(v - y)
+        if best is None or dist < best[0] or (dist == best[0] and c % 2 == 0):
+            best = (dist, c)
+    return best[1]
+
+
+def quantize_block_e2m1(values):
+    """One 32-element MXFP4 block of float values -> (codes, scale byte)."""
+    a = max(abs(x) for x in values)
+    X = -127 if a == 0.0 else max(-127, min(127, floor_log2(a) - 2))
+    codes = []
+    for x in values:
+        y = x / 2.0 ** X
+        y = math.copysign(min(abs(y), 6.0), y)
+        codes.append(nearest_code(y, range(16), e2m1_value))
+    return codes, X + 127
+
+
+def quantize_tile_e4m3(values):
+    """A flat list of tile values -> (E4M3 codes, E8M0 scale byte)."""
+    a = max(abs(x) for x in values)
+    X = -127 if a == 0.0 else max(-127, min(127, floor_log2(a) - 8))
+    codes = []
+    for x in values:
+        y = x / 2.0 ** X
+        y = math.copysign(min(abs(y), 448.0), y)
+        codes.append(nearest_code(y, range(256), e4m3_value))
+    return codes, X + 127
+
+
+def attention_rows(q, k, v, sigma, causal):
+    """q: list of Nq rows, k/v: lists of Nk rows (floats).  Bottom-right
+    causal mask when ``causal``.  Returns (o rows, lse list)."""
+    nq, nk = len(q), len(k)
+    out, lses = [], []
+    for i in range(nq):
+        last = i + (nk - nq) if causal else nk - 1
+        s = [sigma * math.fsum(a * b for a, b in zip(q[i], k[j])) for j in range(last + 1)]
+        m = max(s)
+        p = [math.exp(x - m) for x in s]
+        l = math.fsum(p)
+        out.append([math.fsum(p[j] * v[j][c] for j in range(len(p))) / l for c in range(len(v[0]))])
+        lses.append(m + math.log(l))
+    return out, lses
