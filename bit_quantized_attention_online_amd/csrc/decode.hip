@@ -1,0 +1,359 @@
+// QK4V8 decode / block-verify attention over a quantized KV cache (gfx950).
+//
+// "MpFA免训练量化：QK4V8混合精度在Blackwell上的推理加速实践" §1.3: decode attention
+// is memory-bound and 4-bit K cuts its traffic; §6.1: pair it with a quantized
+// KV cache.  "小米MiMo-V2.5-Pro-FP4-DFlash：FP4+推测解码的万亿推理提速指南", section
+// "DFlash块扩散推测解码": a drafted block of tokens is verified by one backbone
+// pass, i.e. q_len queries with a bottom-right causal mask over the cache.
+//
+// Split-K: one workgroup per (batch, KV head, split of the KV range).  The
+// G*q_len query rows of a KV head (G = q_heads / kv_heads) form up to four
+// 16-row blocks, one wave each; every wave streams the same 128-key tiles
+// through LDS:
+//   K codes (row-major, padded rows) -> QK^T A operand (16 B per lane),
+//   V codes (row-major, 16-byte chunks XOR-swizzled by row) -> ds_read_tr8_b64
+//   gathers 8 keys of one column per lane, which is the P·V A operand layout.
+// Each split writes its normalized fp32 partial output and log2-sum-exp; the
+// merge kernel combines splits with log-sum-exp weights.
+#include "qk4v8_device.h"
+#include "qk4v8_launch.h"
+
+namespace qk4v8 {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyRescale = 8.0f;
+
+__host__ __device__ constexpr int subtile_key(int t, int r) {
+  return (t >> 2) * 64 + 16 * (r >> 2) + 4 * (t & 3) + (r & 3);
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef v2i __attribute__((address_space(3))) * lds_v2i_ptr;
+
+}  // namespace
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint8_t* kc;
+  const uint8_t* ksc;
+  const uint8_t* vc;
+  const uint8_t* vsc;
+  const int32_t* kv_lens;
+  float* part_o;      // [bk][split][M][D]
+  float* part_lse;    // [bk][split][M]  (log2 domain)
+  int64_t qs0, qs1, qs2;
+  int kv_heads, group, q_len, M, kv_len, cap, R, splits, tiles_per_split;
+  int64_t n_vtiles_cap;
+  float c;
+};
+
+template <int D>
+struct DecTile {
+  static constexpr int NB = D / 32;             // MXFP4 blocks per key
+  static constexpr int NC = D / 16;             // 16-byte V chunks per key
+  static constexpr int KRB = D / 2 + 16;        // padded K row bytes in LDS
+  static constexpr int K = 128 * KRB;
+  static constexpr int KS = 128 * 4;            // one dword of scales per key
+  static constexpr int V = 128 * D;
+  static constexpr int BYTES = K + KS + V;
+};
+
+template <int D>
+__device__ __forceinline__ int vswz(int row, int chunk) {
+  return chunk ^ (row & (DecTile<D>::NC - 1));
+}
+
+template <int D, int MB>
+__global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
+  using T = DecTile<D>;
+  constexpr int NB = T::NB, NC = T::NC, ND = D / 16;
+  constexpr int NT = MB * 64;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[T::BYTES];
+  uint8_t* lk = lds;
+  uint8_t* lks = lds + T::K;
+  uint8_t* lv = lds + T::K + T::KS;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 15, lg = lane >> 4;
+  const int s = blockIdx.x % a.splits;
+  const int64_t bk = blockIdx.x / a.splits;
+  const int b = (int)(bk / a.kv_heads), kvh = (int)(bk - (int64_t)b * a.kv_heads);
+  const int kvlen = a.kv_lens ? a.kv_lens[b] : a.kv_len;
+  const int j_begin = s * a.tiles_per_split * 128;
+  const int j_end = min(kvlen, j_begin + a.tiles_per_split * 128);
+  const int ntiles = j_end > j_begin ? (j_end - j_begin + 127) / 128 : 0;
+
+  // ---- this wave's 16 query rows: row m = t * G + (head within group) ----
+  const int mrow = wave * 16 + ql;
+  const bool row_ok = mrow < a.M;
+  const int qt = row_ok ? mrow / a.group : 0;
+  const int head = kvh * a.group + (row_ok ? mrow - qt * a.group : 0);
+  const int lim = row_ok ? kvlen - a.q_len + qt : -1;   // last visible key
+  v8i qf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  int qsc = 127;
+  if (row_ok && lg < NB) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.q + b * a.qs0 + qt * a.qs1 + (int64_t)head * a.qs2 + 32 * lg);
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 x = src[i];
+      w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+    }
+    uint32_t cq[4];
+    qsc = (int)mxfp4_quantize32(w, cq);
+    qf[0] = (int)cq[0]; qf[1] = (int)cq[1]; qf[2] = (int)cq[2]; qf[3] = (int)cq[3];
+  }
+
+  v4f O[ND];
+#pragma unroll
+  for (int dd = 0; dd < ND; ++dd) O[dd] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  const uint8_t* gk = a.kc + bk * (int64_t)a.cap * (D / 2);
+  const uint32_t* gks = reinterpret_cast<const uint32_t*>(a.ksc + bk * (int64_t)a.cap * NB);
+  const uint8_t* gv = a.vc + bk * (int64_t)a.cap * D;
+  const uint8_t* gvs = a.vsc + bk * a.n_vtiles_cap;
+
+  // ---- tile staging (registers hold the next tile while this one computes) ----
+  constexpr int KCH = 128 * NB;          // 16-byte K chunks per tile
+  constexpr int VCH = 128 * NC;          // 16-byte V chunks per tile
+  constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VCH + NT - 1) / NT, SPT = (128 + NT - 1) / NT;
+  uint4 rk[KPT], rv[VPT];
+  uint32_t rs[SPT];
+  auto gload = [&](int tile) {
+    const int j0 = j_begin + tile * 128;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int ci = tid + i * NT;
+      if (ci < KCH) {
+        const int key = min(j0 + ci / NB, a.cap - 1);
+        rk[i] = *reinterpret_cast<const uint4*>(gk + (int64_t)key * (D / 2) + (ci % NB) * 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int ci = tid + i * NT;
+      if (ci < VCH) {
+        const int key = min(j0 + ci / NC, a.cap - 1);
+        rv[i] = *reinterpret_cast<const uint4*>(gv + (int64_t)key * D + (ci % NC) * 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int ki = tid + i * NT;
+      if (ki < 128) {
+        const int key = min(j0 + ki, a.cap - 1);
+        rs[i] = NB == 4 ? gks[key] : (uint32_t)reinterpret_cast<const uint16_t*>(gks)[key];
+      }
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int ci = tid + i * NT;
+      if (ci < KCH) *reinterpret_cast<uint4*>(lk + (ci / NB) * T::KRB + (ci % NB) * 16) = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int ci = tid + i * NT;
+      if (ci < VCH) {
+        const int row = ci / NC;
+        *reinterpret_cast<uint4*>(lv + row * D + vswz<D>(row, ci % NC) * 16) = rv[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int ki = tid + i * NT;
+      if (ki < 128) reinterpret_cast<uint32_t*>(lks)[ki] = rs[i];
+    }
+  };
+
+  if (ntiles > 0) gload(0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = j_begin + it * 128;
+    __syncthreads();            // previous tile fully consumed
+    sstore();
+    __syncthreads();            // this tile visible
+    if (it + 1 < ntiles) gload(it + 1);
+
+    // ---- S^T = K · Q^T ----
+    v4f S[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int key = subtile_key(t, ql);
+      v8i af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      int sa = 127;
+      if (lg < NB) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(lk + key * T::KRB + lg * 16);
+        af[0] = (int)kv.x; af[1] = (int)kv.y; af[2] = (int)kv.z; af[3] = (int)kv.w;
+        sa = (int)((reinterpret_cast<const uint32_t*>(lks)[key] >> (8 * lg)) & 0xFF);
+      }
+      S[t] = mfma16x16x128<kFmtFp4, kFmtFp4>(af, qf, v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc);
+    }
+    // ---- mask: keys past this row's limit (covers kv_len and the causal block) ----
+    if (j0 + 127 > kvlen - a.q_len || !row_ok) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (j0 + subtile_key(t, 4 * lg + i) > lim) S[t][i] = -INFINITY;
+    }
+    // ---- online softmax + two-term FP8 P ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float tmax = mx * a.c;
+    const float m_new = fmaxf(m_run, tmax);
+    if (__any(m_new > m_run + kLazyRescale)) {
+      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int dd = 0; dd < ND; ++dd) O[dd] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
+    const float sh = exp2i(X), sl = exp2i(X - 4);
+    v8i Phi, Plo;
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(S[t][i], a.c, -m_use));
+      lsum += (p[0] + p[1]) + (p[2] + p[3]);
+      const uint32_t h01 = e4m3_pack2(p[0], p[1], sh);
+      const uint32_t h23 = e4m3_pack2(p[2], p[3], sh);
+      const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h01, sh, false);
+      const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h23, sh, false);
+      const uint32_t l01 = e4m3_pack2(p[0] - b01[0], p[1] - b01[1], sl);
+      const uint32_t l23 = e4m3_pack2(p[2] - b23[0], p[3] - b23[1], sl);
+      Phi[t] = (int)(h01 | (h23 << 16));
+      Plo[t] = (int)(l01 | (l23 << 16));
+    }
+    l_part += lsum;
+    // ---- O^T += V^T · P^T ----
+    const int vkey = min(j0 + 32 * lg, a.cap - 1);
+    const int vs = (int)gvs[vkey / a.R];
+    const int src_row_in_piece = ql >> 1, src_half = ql & 1;
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) {
+      v8i av;
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        const int row = (pc >> 1) * 64 + 16 * lg + (pc & 1) * 8 + src_row_in_piece;
+        const int addr = row * D + vswz<D>(row, dd) * 16 + src_half * 8;
+        const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)(lv + addr));
+        av[2 * pc] = r[0];
+        av[2 * pc + 1] = r[1];
+      }
+      O[dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(av, Phi, O[dd], vs, X + 127);
+      O[dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(av, Plo, O[dd], vs, X + 123);
+    }
+  }
+
+  // ---- write this split's normalized partial and its log2-sum-exp ----
+  float l = l_part;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!row_ok) return;
+  const int64_t prow = (bk * a.splits + s) * a.M + mrow;
+  const bool empty = !(l > 0.0f);
+  const float inv = empty ? 0.0f : 1.0f / l;
+  float* dst = a.part_o + prow * D;
+#pragma unroll
+  for (int dd = 0; dd < ND; ++dd) *reinterpret_cast<v4f*>(dst + dd * 16 + 4 * lg) = O[dd] * inv;
+  if (lg == 0) a.part_lse[prow] = empty ? -INFINITY : (m_run + __log2f(l));
+}
+
+// One workgroup of D threads per (batch, KV head, query row): combine the
+// splits' partials with weights 2^(lse_s - max).
+template <int D>
+__global__ void __launch_bounds__(D) decode_merge_kernel(const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_lse, int kv_heads, int group,
+                                                         int M, int splits, uint16_t* __restrict__ o, int64_t os0,
+                                                         int64_t os1, int64_t os2, float* __restrict__ lse,
+                                                         int q_heads, int q_len) {
+  const int64_t r = blockIdx.x;               // (bk, mrow)
+  const int64_t bk = r / M;
+  const int mrow = (int)(r - bk * M);
+  const int b = (int)(bk / kv_heads), kvh = (int)(bk - (int64_t)b * kv_heads);
+  const int qt = mrow / group, head = kvh * group + (mrow - qt * group);
+  const float* pl = part_lse + bk * splits * M + mrow;
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, pl[(int64_t)s * M]);
+  float wsum = 0.f, acc = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f(pl[(int64_t)s * M] - mx);
+      wsum += w;
+      acc += w * part_o[((bk * splits + s) * M + mrow) * D + threadIdx.x];
+    }
+  }
+  const float val = wsum > 0.f ? acc / wsum : 0.f;
+  o[b * os0 + qt * os1 + (int64_t)head * os2 + threadIdx.x] = (uint16_t)f32_to_bf16(val);
+  if (lse != nullptr && threadIdx.x == 0)
+    lse[((int64_t)b * q_len + qt) * q_heads + head] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+int decode_num_splits(int batch, int kv_heads, int kv_len, int requested) {
+  const int tiles = (kv_len + 127) / 128;
+  if (requested > 0) return requested < tiles ? requested : tiles;
+  // aim for >= 2048 workgroups in flight, each with >= 4 tiles of work
+  const int64_t units = (int64_t)batch * kv_heads;
+  int s = (int)((2048 + units - 1) / units);
+  const int max_s = tiles / 4 > 0 ? tiles / 4 : 1;
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  return s;
+}
+
+size_t decode_workspace_bytes(int batch, int q_len, int q_heads, int kv_heads, int head_dim, int splits) {
+  const size_t M = (size_t)(q_heads / kv_heads) * q_len;
+  const size_t rows = (size_t)batch * kv_heads * splits * M;
+  const size_t o_bytes = (rows * head_dim * 4 + kWsAlign - 1) / kWsAlign * kWsAlign;
+  return o_bytes + (rows * 4 + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
+  DecodeArgs a;
+  const int G = p.q_heads / p.kv_heads;
+  const int M = G * p.q_len;
+  const int splits = decode_num_splits(p.batch, p.kv_heads, p.kv_len, p.num_splits);
+  const int tiles = (p.kv_len + 127) / 128;
+  a.q = p.q; a.kc = p.k_codes; a.ksc = p.k_scales; a.vc = p.v_codes; a.vsc = p.v_scales; a.kv_lens = p.kv_lens;
+  const size_t rows = (size_t)p.batch * p.kv_heads * splits * M;
+  a.part_o = reinterpret_cast<float*>(p.ws);
+  a.part_lse = reinterpret_cast<float*>(p.ws + (rows * D * 4 + kWsAlign - 1) / kWsAlign * kWsAlign);
+  a.qs0 = p.qs[0]; a.qs1 = p.qs[1]; a.qs2 = p.qs[2];
+  a.kv_heads = p.kv_heads; a.group = G; a.q_len = p.q_len; a.M = M; a.kv_len = p.kv_len; a.cap = p.cap;
+  a.R = p.v_tile_rows; a.splits = splits; a.tiles_per_split = (tiles + splits - 1) / splits;
+  a.n_vtiles_cap = (p.cap + p.v_tile_rows - 1) / p.v_tile_rows;
+  a.c = p.softmax_scale * kLog2e;
+  const dim3 grid((unsigned)((int64_t)p.batch * p.kv_heads * splits));
+  const int MB = (M + 15) / 16;
+  switch (MB) {
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, dim3(128), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((decode_split_kernel<D, 3>), grid, dim3(192), 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, 4>), grid, dim3(256), 0, stream, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((int64_t)p.batch * p.kv_heads * M)), dim3(D), 0,
+                     stream, a.part_o, a.part_lse, p.kv_heads, G, M, splits, p.o, p.os[0], p.os[1], p.os[2], p.lse,
+                     p.q_heads, p.q_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  return p.head_dim == 64 ? launch_decode_d<64>(p, stream) : launch_decode_d<128>(p, stream);
+}
+
+}  // namespace qk4v8

@@ -1,0 +1,207 @@
+// C-ABI host layer of libqk4v8: argument validation, device check, launches.
+//
+// The MpFA page ("MpFA免训练量化：QK4V8混合精度在Blackwell上的推理加速实践") §4.2
+// and §5.2 warn that a Q/K/V stride or layout mismatch shows up as an illegal
+// memory access; every size, stride and alignment is therefore checked on the
+// host before anything is enqueued, and a failed check returns a status.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/qk4v8.h"
+#include "qk4v8_launch.h"
+
+using namespace qk4v8;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_v_tile(int r) { return r == 32 || r == 64 || r == 128 || r == 256; }
+
+// gfx950 check, memoised per device ordinal (the only state the library keeps).
+qk4v8_status check_device() {
+  static std::atomic<int> verdict[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QK4V8_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    const int v = verdict[dev].load(std::memory_order_relaxed);
+    if (v == 1) return QK4V8_OK;
+    if (v == 2) return QK4V8_ERR_UNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QK4V8_ERR_HIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) verdict[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? QK4V8_OK : QK4V8_ERR_UNSUPPORTED;
+}
+
+qk4v8_status from_hip(hipError_t e) { return e == hipSuccess ? QK4V8_OK : QK4V8_ERR_HIP; }
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+
+qk4v8_status validate_prefill(const qk4v8_prefill_args* a) {
+  if (a == nullptr) return QK4V8_ERR_NULL;
+  if (a->batch < 0 || a->q_heads < 1 || a->kv_heads < 1 || a->seq_q < 0 || a->seq_k < 0) return QK4V8_ERR_SHAPE;
+  if (a->q_heads % a->kv_heads != 0) return QK4V8_ERR_SHAPE;
+  if (a->head_dim != 64 && a->head_dim != 128) return QK4V8_ERR_SHAPE;
+  if (!valid_v_tile(a->v_tile_rows)) return QK4V8_ERR_SHAPE;
+  if (a->causal != 0 && a->causal != 1) return QK4V8_ERR_SHAPE;
+  if (a->seq_q > 0 && a->seq_k < 1) return QK4V8_ERR_SHAPE;
+  if (a->causal && a->seq_q > a->seq_k) return QK4V8_ERR_SHAPE;
+  if (!good_scale(a->softmax_scale)) return QK4V8_ERR_SHAPE;
+  if (a->seq_q > (1 << 30) || a->seq_k > (1 << 30)) return QK4V8_ERR_SHAPE;
+  return QK4V8_OK;
+}
+
+qk4v8_status validate_prefill_memory(const qk4v8_prefill_args* a) {
+  if (!a->q || !a->k || !a->v || !a->o) return QK4V8_ERR_NULL;
+  const int64_t* strides[4] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
+  for (auto s : strides)
+    for (int i = 0; i < 3; ++i)
+      if (s[i] < 0 || s[i] % 8 != 0) return QK4V8_ERR_STRIDE;
+  if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->o, 16)) return QK4V8_ERR_STRIDE;
+  if (a->lse && !aligned(a->lse, 4)) return QK4V8_ERR_STRIDE;
+  // rows of one head must not overlap, nor may heads of the output
+  const int d = a->head_dim;
+  if (a->seq_q > 1 && (a->q_stride[2] < d || a->o_stride[2] < d)) return QK4V8_ERR_STRIDE;
+  if (a->seq_k > 1 && (a->k_stride[2] < d || a->v_stride[2] < d)) return QK4V8_ERR_STRIDE;
+  if (a->q_heads > 1 && a->o_stride[1] < d) return QK4V8_ERR_STRIDE;
+  if (a->workspace == nullptr || !aligned(a->workspace, kWsAlign)) return QK4V8_ERR_WORKSPACE;
+  const PrefillLayout L = prefill_layout(a->batch, a->kv_heads, a->seq_k, a->head_dim, a->v_tile_rows);
+  if (a->workspace_bytes < L.total) return QK4V8_ERR_WORKSPACE;
+  return QK4V8_OK;
+}
+
+qk4v8_status validate_decode(const qk4v8_decode_args* a) {
+  if (a == nullptr) return QK4V8_ERR_NULL;
+  if (a->batch < 0 || a->q_heads < 1 || a->kv_heads < 1 || a->q_len < 1) return QK4V8_ERR_SHAPE;
+  if (a->q_heads % a->kv_heads != 0) return QK4V8_ERR_SHAPE;
+  if (a->head_dim != 64 && a->head_dim != 128) return QK4V8_ERR_SHAPE;
+  if (!valid_v_tile(a->v_tile_rows)) return QK4V8_ERR_SHAPE;
+  if (a->kv_len < a->q_len || a->cap < a->kv_len || a->cap > (1 << 30)) return QK4V8_ERR_SHAPE;
+  if ((int64_t)(a->q_heads / a->kv_heads) * a->q_len > 64) return QK4V8_ERR_SHAPE;
+  if (a->num_splits < 0) return QK4V8_ERR_SHAPE;
+  if (!good_scale(a->softmax_scale)) return QK4V8_ERR_SHAPE;
+  return QK4V8_OK;
+}
+
+int decode_splits(const qk4v8_decode_args* a) {
+  return decode_num_splits(a->batch, a->kv_heads, a->kv_len, a->num_splits);
+}
+
+qk4v8_status validate_decode_memory(const qk4v8_decode_args* a) {
+  if (!a->q || !a->k_codes || !a->k_scales || !a->v_codes || !a->v_scales || !a->o) return QK4V8_ERR_NULL;
+  for (int i = 0; i < 3; ++i)
+    if (a->q_stride[i] < 0 || a->q_stride[i] % 8 != 0 || a->o_stride[i] < 0) return QK4V8_ERR_STRIDE;
+  if (!aligned(a->q, 16) || !aligned(a->o, 2) || !aligned(a->k_codes, 16) || !aligned(a->v_codes, 16))
+    return QK4V8_ERR_STRIDE;
+  if (!aligned(a->k_scales, a->head_dim == 128 ? 4 : 2)) return QK4V8_ERR_STRIDE;
+  if (a->kv_lens && !aligned(a->kv_lens, 4)) return QK4V8_ERR_STRIDE;
+  if (a->lse && !aligned(a->lse, 4)) return QK4V8_ERR_STRIDE;
+  if (a->q_heads > 1 && a->o_stride[2] < a->head_dim) return QK4V8_ERR_STRIDE;
+  if (a->q_len > 1 && a->o_stride[1] < a->head_dim) return QK4V8_ERR_STRIDE;
+  if (a->workspace == nullptr || !aligned(a->workspace, kWsAlign)) return QK4V8_ERR_WORKSPACE;
+  const size_t need =
+      decode_workspace_bytes(a->batch, a->q_len, a->q_heads, a->kv_heads, a->head_dim, decode_splits(a));
+  if (a->workspace_bytes < need) return QK4V8_ERR_WORKSPACE;
+  return QK4V8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qk4v8_abi_version(void) { return QK4V8_ABI_VERSION; }
+
+const char* qk4v8_status_string(int status) {
+  switch (status) {
+    case QK4V8_OK: return "ok";
+    case QK4V8_ERR_NULL: return "null pointer";
+    case QK4V8_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case QK4V8_ERR_STRIDE: return "misaligned pointer or invalid stride";
+    case QK4V8_ERR_UNSUPPORTED: return "device is not gfx950";
+    case QK4V8_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case QK4V8_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+qk4v8_status qk4v8_quantize_qk(const uint16_t* x, int64_t rows, int32_t d, int64_t ld, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream) {
+  if (rows < 0 || d <= 0 || d % 32 != 0 || d > 1024) return QK4V8_ERR_SHAPE;
+  if (rows > ((int64_t)1 << 40) / d) return QK4V8_ERR_SHAPE;
+  if (ld < d || ld % 8 != 0) return QK4V8_ERR_STRIDE;
+  if (rows == 0) return QK4V8_OK;
+  if (!x || !codes || !scales) return QK4V8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 4)) return QK4V8_ERR_STRIDE;
+  if ((rows * (d / 8) + 255) / 256 > 0x7FFFFFFF) return QK4V8_ERR_SHAPE;
+  qk4v8_status st = check_device();
+  if (st != QK4V8_OK) return st;
+  return from_hip(launch_quantize_qk(x, rows, d, ld, codes, scales, stream));
+}
+
+qk4v8_status qk4v8_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int32_t d, int64_t group_stride,
+                              int64_t row_stride, int32_t tile_rows, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream) {
+  if (groups < 0 || n < 0 || d <= 0 || d % 8 != 0 || d > 512 || !valid_v_tile(tile_rows)) return QK4V8_ERR_SHAPE;
+  if (row_stride < d || row_stride % 8 != 0 || group_stride < 0 || group_stride % 8 != 0) return QK4V8_ERR_STRIDE;
+  if (groups == 0 || n == 0) return QK4V8_OK;
+  if (!v || !codes || !scales) return QK4V8_ERR_NULL;
+  if (!aligned(v, 16) || !aligned(codes, 8)) return QK4V8_ERR_STRIDE;
+  if (groups * ((n + tile_rows - 1) / tile_rows) > 0x7FFFFFFF) return QK4V8_ERR_SHAPE;
+  qk4v8_status st = check_device();
+  if (st != QK4V8_OK) return st;
+  return from_hip(launch_quantize_v(v, groups, n, d, group_stride, row_stride, tile_rows, codes, scales, stream));
+}
+
+size_t qk4v8_prefill_workspace_bytes(const qk4v8_prefill_args* a) {
+  if (validate_prefill(a) != QK4V8_OK) return 0;
+  return prefill_layout(a->batch, a->kv_heads, a->seq_k, a->head_dim, a->v_tile_rows).total;
+}
+
+qk4v8_status qk4v8_attn_prefill(const qk4v8_prefill_args* a, hipStream_t stream) {
+  qk4v8_status st = validate_prefill(a);
+  if (st != QK4V8_OK) return st;
+  if (a->batch == 0 || a->seq_q == 0) return QK4V8_OK;
+  st = validate_prefill_memory(a);
+  if (st != QK4V8_OK) return st;
+  st = check_device();
+  if (st != QK4V8_OK) return st;
+  PrefillParams p;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.lse = a->lse;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = a->q_stride[i]; p.ks[i] = a->k_stride[i]; p.vs[i] = a->v_stride[i]; p.os[i] = a->o_stride[i];
+  }
+  p.batch = a->batch; p.q_heads = a->q_heads; p.kv_heads = a->kv_heads; p.seq_q = a->seq_q; p.seq_k = a->seq_k;
+  p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows; p.causal = a->causal;
+  p.softmax_scale = a->softmax_scale;
+  p.ws = static_cast<uint8_t*>(a->workspace);
+  return from_hip(launch_prefill(p, stream));
+}
+
+size_t qk4v8_decode_workspace_bytes(const qk4v8_decode_args* a) {
+  if (validate_decode(a) != QK4V8_OK) return 0;
+  return decode_workspace_bytes(a->batch, a->q_len, a->q_heads, a->kv_heads, a->head_dim, decode_splits(a));
+}
+
+qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream) {
+  qk4v8_status st = validate_decode(a);
+  if (st != QK4V8_OK) return st;
+  if (a->batch == 0) return QK4V8_OK;
+  st = validate_decode_memory(a);
+  if (st != QK4V8_OK) return st;
+  st = check_device();
+  if (st != QK4V8_OK) return st;
+  DecodeParams p;
+  p.q = a->q; p.k_codes = a->k_codes; p.k_scales = a->k_scales; p.v_codes = a->v_codes; p.v_scales = a->v_scales;
+  p.kv_lens = a->kv_lens; p.o = a->o; p.lse = a->lse;
+  for (int i = 0; i < 3; ++i) { p.qs[i] = a->q_stride[i]; p.os[i] = a->o_stride[i]; }
+  p.batch = a->batch; p.q_len = a->q_len; p.q_heads = a->q_heads; p.kv_heads = a->kv_heads; p.kv_len = a->kv_len;
+  p.cap = a->cap; p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows;
+  p.num_splits = a->num_splits; p.softmax_scale = a->softmax_scale;
+  p.ws = static_cast<uint8_t*>(a->workspace);
+  return from_hip(launch_decode(p, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qk4v8 {
+
+constexpr int kKvTile = 128;    // keys per attention KV tile
+constexpr int kWsAlign = 256;   // workspace sub-buffer alignment (bytes)
+
+hipError_t launch_quantize_qk(const uint16_t* x, int64_t rows, int d, int64_t ld, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream);
+hipError_t launch_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int d, int64_t group_stride,
+                             int64_t row_stride, int R, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+// Prefill: the quantized copies of K and V live in the caller's workspace in
+// the layouts the attention kernel consumes (see prefill.hip).
+struct PrefillLayout {
+  int64_t n_tiles;        // ceil(seq_k / 128)
+  int64_t n_vtiles;       // ceil(seq_k / v_tile_rows)
+  size_t off_k, off_ks, off_v, off_vs, off_vtile, total;
+};
+PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, int v_tile_rows);
+
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int batch, q_heads, kv_heads, seq_q, seq_k, head_dim, v_tile_rows, causal;
+  float softmax_scale;
+  uint8_t* ws;
+};
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const int32_t* kv_lens;
+  uint16_t* o;
+  float* lse;
+  int64_t qs[3], os[3];
+  int batch, q_len, q_heads, kv_heads, kv_len, cap, head_dim, v_tile_rows, num_splits;
+  float softmax_scale;
+  uint8_t* ws;
+};
+int decode_num_splits(int batch, int kv_heads, int kv_len, int requested);
+size_t decode_workspace_bytes(int batch, int q_len, int q_heads, int kv_heads, int head_dim, int splits);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace qk4v8

@@ -15,6 +15,8 @@ tensor_id, b, h])`` so that one (batch, head) slice can be regenerated alone.
 tensor_id: 0 = Q, 1 = K, 2 = V, 3 = outlier selection.
 """
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 ROOT_SEED = 20261203
@@ -23,8 +25,9 @@ Q_ID, K_ID, V_ID, OUTLIER_ID = 0, 1, 2, 3
 
 def bf16_bits(x):
     """float32 array -> bfloat16 bit patterns (uint16), round-to-nearest-even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    one, half = np.uint32(1), np.uint32(0x7FFF)      # finite inputs: no uint32 overflow
+    return ((u + half + ((u >> np.uint32(16)) & one)) >> np.uint32(16)).astype(np.uint16)
 
 
 def bits_to_f32(bits):
@@ -44,12 +47,29 @@ def normal_bits(cfg, tensor_id, b, h, shape, scale=1.0):
     return bf16_bits(x)
 
 
-def normal_tensor(cfg, tensor_id, B, H, n, d, scale=1.0):
-    """[B, H, n, d] bf16 bits, one independent seeded stream per (b, h)."""
+def normal_tensor(cfg, tensor_id, B, H, n, d, scale=1.0, threads=8):
+    """[B, H, n, d] bf16 bits, one independent seeded stream per (b, h)
+    (slices are drawn in parallel threads; the result does not depend on it)."""
     out = np.empty((B, H, n, d), dtype=np.uint16)
-    for b in range(B):
-        for h in range(H):
-            out[b, h] = normal_bits(cfg, tensor_id, b, h, (n, d), scale)
+
+    def fill(bh):
+        b, h = divmod(bh, H)
+        out[b, h] = normal_bits(cfg, tensor_id, b, h, (n, d), scale)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fill, range(B * H)))
+    return out
+
+
+def normal_batch(cfg, tensor_id, b, H, n, d, threads=8):
+    """[H, n, d] bf16 bits: the slices (b, 0..H-1) of ``normal_tensor``."""
+    out = np.empty((H, n, d), dtype=np.uint16)
+
+    def fill(h):
+        out[h] = normal_bits(cfg, tensor_id, b, h, (n, d))
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fill, range(H)))
     return out
 
 

@@ -1,0 +1,201 @@
+/*
+ * qk4v8.h - C ABI of the QK4V8 attention library for MI355X (gfx950).
+ *
+ * QK4V8 is the training-free mixed-precision attention of the page
+ * "MpFA免训练量化：QK4V8混合精度在Blackwell上的推理加速实践" (mhpn.cn/news/2564245,
+ * below "MpFA page"): Q and K are quantized to 4 bits and V to 8 bits (§1.1,
+ * §2.1, §2.2), each block's scale is computed at run time from the block itself
+ * with no calibration data (§1.2, §3.2), and attention runs as a tiled online
+ * softmax with an FP32 accumulator whose result is cast back to 16 bits (§2.3,
+ * §3.3).  The 4-bit format is MXFP4: E2M1 values sharing one E8M0 scale per 32
+ * elements, the block size named in "小米MiMo-V2.5-Pro-FP4-DFlash：FP4+推测解码的
+ * 万亿推理提速指南" (wmrh.cn/news/72329, below "MiMo page"), section
+ * "MXFP4专家量化".  V is FP8 E4M3FN with one power-of-two (E8M0) scale per tile of
+ * rows.  The MpFA page §4.2 describes shipping the kernel as a standalone
+ * extension whose Q/K/V strides must match the caller's layout; §5.2 lists a
+ * stride mismatch as the cause of illegal memory accesses, so every stride is
+ * validated here before any launch.
+ *
+ * Formats (bit layouts of the OCP MX v1.0 / OFP8 specifications):
+ *   bf16 input        : uint16 bit patterns.
+ *   MXFP4 codes       : uint8, two E2M1 codes per byte; byte k of a row holds
+ *                       element 2k in its low nibble and element 2k+1 in its
+ *                       high nibble.
+ *   MXFP4 scales      : uint8 E8M0, one per 32 consecutive elements of a row;
+ *                       byte b means 2^(b-127).  X = floor(log2 amax) - 2,
+ *                       clamped to [-127, 127]; an all-zero block has b = 0.
+ *   FP8 V codes       : uint8 E4M3FN, one per element.
+ *   FP8 V scales      : uint8 E8M0, one per tile of `tile_rows` rows of one
+ *                       (batch, kv-head); X = floor(log2 amax) - 8.
+ *   Rounding          : round to nearest, ties to even, after saturating the
+ *                       magnitude to the format's largest finite value (6 for
+ *                       E2M1, 448 for E4M3FN).  The sign bit of a value that
+ *                       rounds to zero is kept.
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers; the caller owns every buffer,
+ *     including the workspace sized by the *_workspace_bytes queries.  The
+ *     library allocates no device memory and keeps no state between calls
+ *     (nothing is calibrated or cached).
+ *   - Work is enqueued on `stream` and is asynchronous; the library never
+ *     synchronizes the host.
+ *   - Arguments are validated on the host before any launch; a failed check
+ *     returns its status and enqueues nothing.  Nothing is printed and no
+ *     C++ exception crosses the ABI.  A launch failure returns QK4V8_ERR_HIP.
+ *   - NaN or Inf inputs are outside the contract.
+ *   - The same inputs give the same bits on the same device.
+ *   - Element strides are in elements of the pointed-to type; the innermost
+ *     stride is always 1.  Row strides and base pointers of bf16 inputs must be
+ *     16-byte aligned (row stride a multiple of 8 elements).
+ */
+#ifndef QK4V8_H
+#define QK4V8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QK4V8_ABI_VERSION 1
+
+typedef enum {
+  QK4V8_OK = 0,
+  QK4V8_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  QK4V8_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be,
+                                or outside the supported set                    */
+  QK4V8_ERR_STRIDE = 3,      /* a stride or pointer is misaligned or overlaps  */
+  QK4V8_ERR_UNSUPPORTED = 4, /* the current device is not gfx950               */
+  QK4V8_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required        */
+  QK4V8_ERR_HIP = 6          /* a HIP launch or query failed                   */
+} qk4v8_status;
+
+/* Version of this ABI (QK4V8_ABI_VERSION of the library that was built). */
+int qk4v8_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* qk4v8_status_string(int status);
+
+/*
+ * MXFP4 quantizer, the online per-block scale of MpFA page §3.2 applied to Q
+ * or K along head_dim (blocks of 32 per the MiMo page, "MXFP4专家量化").
+ *   x      : bf16 [rows, d], row stride `ld` elements (ld >= d, ld % 8 == 0).
+ *   codes  : out, uint8 [rows, d/2], contiguous.
+ *   scales : out, uint8 [rows, d/32], contiguous.
+ *   d      : multiple of 32, at most 1024.  rows >= 0 (0 is a no-op).
+ */
+qk4v8_status qk4v8_quantize_qk(const uint16_t* x, int64_t rows, int32_t d, int64_t ld,
+                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/*
+ * FP8 E4M3FN quantizer for V with one E8M0 scale per tile of `tile_rows` rows
+ * (MpFA page §2.2 keeps V at 8 bits; the per-tile scale is the online block
+ * scale of §3.2).
+ *   v            : bf16, element (g, i, c) at v[g*group_stride + i*row_stride + c]
+ *                  (row_stride >= d, both multiples of 8).
+ *   groups       : number of (batch, kv-head) pairs, >= 0.
+ *   n            : rows per group, >= 0.  The last tile of a group may be
+ *                  shorter than tile_rows.
+ *   d            : multiple of 8, at most 512.
+ *   tile_rows    : one of 32, 64, 128, 256.
+ *   codes        : out, uint8 [groups, n, d], contiguous.
+ *   scales       : out, uint8 [groups, ceil(n / tile_rows)], contiguous.
+ */
+qk4v8_status qk4v8_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int32_t d,
+                              int64_t group_stride, int64_t row_stride, int32_t tile_rows,
+                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/*
+ * Prefill attention (MpFA page §2.3, §3.3): Q and K are quantized to MXFP4 and
+ * V to FP8 (per-tile E8M0 scale) inside the call, then
+ *   o_i = sum_j softmax_j(softmax_scale * q̂_i·k̂_j) v̂_j
+ * with an FP32 online softmax and FP32 accumulator, stored as bf16.
+ *
+ *   q : bf16 [batch, q_heads, seq_q, head_dim], strides q_stride = {batch, head, token}
+ *   k : bf16 [batch, kv_heads, seq_k, head_dim], strides k_stride
+ *   v : bf16 [batch, kv_heads, seq_k, head_dim], strides v_stride
+ *   o : out bf16 [batch, q_heads, seq_q, head_dim], strides o_stride
+ *   lse : out fp32 [batch, q_heads, seq_q] contiguous, natural-log
+ *         log-sum-exp of the scaled scores of each row; may be NULL.
+ *   head_dim ∈ {64, 128}; q_heads % kv_heads == 0 and query head h reads KV
+ *   head h / (q_heads / kv_heads) (GQA); v_tile_rows ∈ {32, 64, 128, 256};
+ *   causal ∈ {0, 1}: row i sees keys j <= i + seq_k - seq_q (bottom-right),
+ *   and needs seq_q <= seq_k.  seq_k >= 1 when seq_q >= 1.
+ *   softmax_scale: applied in fp32 to the dequantized dot products.
+ *   workspace : device scratch of at least qk4v8_prefill_workspace_bytes()
+ *               bytes, 256-byte aligned; it receives the call's quantized
+ *               copies of K and V.  Contents on return are unspecified.
+ */
+typedef struct {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int32_t batch, q_heads, kv_heads, seq_q, seq_k, head_dim, v_tile_rows, causal;
+  float softmax_scale;
+  void* workspace;
+  size_t workspace_bytes;
+} qk4v8_prefill_args;
+
+/* Workspace bytes qk4v8_attn_prefill needs for these sizes (0 on bad sizes). */
+size_t qk4v8_prefill_workspace_bytes(const qk4v8_prefill_args* a);
+qk4v8_status qk4v8_attn_prefill(const qk4v8_prefill_args* a, hipStream_t stream);
+
+/*
+ * Decode / block-verify attention over a quantized KV cache (MpFA page §1.3:
+ * decode is memory-bound and 4-bit K cuts its traffic; §6.1: combined with a
+ * quantized KV cache).  q_len new query tokens per sequence (1 for decode, or a
+ * drafted block verified in one pass as in the MiMo page, section
+ * "DFlash块扩散推测解码"); query t of the block sees cache keys
+ * j <= kv_len_b - q_len + t (bottom-right causal).  The queries are quantized
+ * to MXFP4 inside the call.  The KV range is split across workgroups and the
+ * partial results merged by log-sum-exp.
+ *
+ *   q        : bf16 [batch, q_len, q_heads, head_dim], strides q_stride = {batch, token, head}
+ *   k_codes  : uint8 [batch, kv_heads, cap, head_dim/2]   (MXFP4, as qk4v8_quantize_qk)
+ *   k_scales : uint8 [batch, kv_heads, cap, head_dim/32]
+ *   v_codes  : uint8 [batch, kv_heads, cap, head_dim]     (E4M3FN, as qk4v8_quantize_v)
+ *   v_scales : uint8 [batch, kv_heads, ceil(cap / v_tile_rows)]
+ *   kv_lens  : device int32 [batch] with q_len <= kv_lens[b] <= kv_len, or NULL
+ *              for every sequence having kv_len entries.
+ *   o        : out bf16 [batch, q_len, q_heads, head_dim], strides o_stride
+ *   lse      : out fp32 [batch, q_len, q_heads] contiguous, natural log; may be NULL.
+ *   head_dim ∈ {64, 128}; v_tile_rows ∈ {32, 64, 128, 256};
+ *   1 <= q_len <= kv_len <= cap; (q_heads / kv_heads) * q_len <= 64.
+ *   num_splits: KV splits per (batch, kv-head), 0 = chosen by the library.
+ *   workspace : at least qk4v8_decode_workspace_bytes() bytes, 256-byte aligned
+ *               (fp32 partial outputs and log-sum-exps of the splits).
+ */
+typedef struct {
+  const uint16_t* q;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const int32_t* kv_lens;
+  uint16_t* o;
+  float* lse;
+  int64_t q_stride[3];
+  int64_t o_stride[3];
+  int32_t batch, q_len, q_heads, kv_heads, kv_len, cap, head_dim, v_tile_rows, num_splits;
+  float softmax_scale;
+  void* workspace;
+  size_t workspace_bytes;
+} qk4v8_decode_args;
+
+/* Workspace bytes qk4v8_attn_decode needs for these sizes (0 on bad sizes). */
+size_t qk4v8_decode_workspace_bytes(const qk4v8_decode_args* a);
+qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QK4V8_H */

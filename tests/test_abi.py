@@ -1,0 +1,118 @@
+"""C-ABI surface on the CPU: the library loads, exports every function that
+include/qk4v8.h declares, and rejects invalid arguments with the documented
+status before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_attention_online_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qk4v8.h")).read()
+    return sorted(set(re.findall(r"\b(qk4v8_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_exported_api():
+    assert _declared() == sorted(ops.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ops.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.qk4v8_abi_version() == 1
+    for s in range(7):
+        assert L.qk4v8_status_string(s)
+
+
+def test_quantize_validation():
+    L = ops.lib()
+    p = ctypes.c_void_p(4096)
+    assert L.qk4v8_quantize_qk(p, 10, 48, 48, p, p, None) == 2          # d % 32
+    assert L.qk4v8_quantize_qk(p, -1, 64, 64, p, p, None) == 2
+    assert L.qk4v8_quantize_qk(p, 10, 64, 60, p, p, None) == 3          # ld < d
+    assert L.qk4v8_quantize_qk(p, 10, 64, 68, p, p, None) == 3          # ld % 8
+    assert L.qk4v8_quantize_qk(None, 10, 64, 64, p, p, None) == 1
+    assert L.qk4v8_quantize_qk(None, 0, 64, 64, None, None, None) == 0  # empty is a no-op
+    assert L.qk4v8_quantize_qk(ctypes.c_void_p(4098), 10, 64, 64, p, p, None) == 3   # misaligned
+    assert L.qk4v8_quantize_v(p, 2, 10, 64, 640, 64, 48, p, p, None) == 2            # tile rows
+    assert L.qk4v8_quantize_v(p, 2, 10, 64, 644, 64, 64, p, p, None) == 3            # group stride % 8
+    assert L.qk4v8_quantize_v(p, 2, 10, 64, 640, 60, 64, p, p, None) == 3            # row stride < d
+    assert L.qk4v8_quantize_v(p, 0, 10, 64, 640, 64, 64, None, None, None) == 0
+
+
+def _prefill(**kw):
+    a = ops.PrefillArgs()
+    a.q = a.k = a.v = a.o = 4096
+    for f in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        getattr(a, f)[:] = [8 * 64 * 128, 64 * 128, 128]
+    a.batch, a.q_heads, a.kv_heads, a.seq_q, a.seq_k, a.head_dim = 1, 8, 2, 64, 64, 128
+    a.v_tile_rows, a.causal, a.softmax_scale = 64, 1, 0.088
+    a.workspace, a.workspace_bytes = 1 << 20, 1 << 30
+    for k, v in kw.items():
+        if k.endswith("stride"):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_heads=6, kv_heads=4), 2), (dict(head_dim=96), 2), (dict(v_tile_rows=100), 2),
+    (dict(causal=2), 2), (dict(seq_q=65), 2), (dict(softmax_scale=0.0), 2), (dict(softmax_scale=float("nan")), 2),
+    (dict(q=None), 1), (dict(q_stride=[64 * 128, 128, 36]), 3), (dict(o_stride=[64 * 128, 128, 4]), 3),
+    (dict(k=4100), 3), (dict(workspace=None), 5), (dict(workspace=1 << 20 | 8), 5), (dict(workspace_bytes=16), 5),
+])
+def test_prefill_validation(kw, status):
+    a = _prefill(**kw)
+    assert ops.lib().qk4v8_attn_prefill(ctypes.byref(a), None) == status
+
+
+def test_prefill_empty_and_workspace_query():
+    L = ops.lib()
+    assert L.qk4v8_attn_prefill(ctypes.byref(_prefill(batch=0, q=None)), None) == 0
+    assert L.qk4v8_attn_prefill(ctypes.byref(_prefill(seq_q=0, causal=0)), None) == 0
+    ws = L.qk4v8_prefill_workspace_bytes(ctypes.byref(_prefill()))
+    # K codes + K scales + V codes + V tile-scale words + per-tile V scales, 256-B aligned
+    assert ws >= 2 * 1 * 128 * (64 + 4 + 128)
+    assert L.qk4v8_prefill_workspace_bytes(ctypes.byref(_prefill(head_dim=96))) == 0
+
+
+def _decode(**kw):
+    a = ops.DecodeArgs()
+    a.q = a.k_codes = a.v_codes = a.o = 4096
+    a.k_scales = a.v_scales = 4096
+    a.q_stride[:] = [64 * 128, 64 * 128, 128]
+    a.o_stride[:] = [64 * 128, 64 * 128, 128]
+    a.batch, a.q_len, a.q_heads, a.kv_heads, a.kv_len, a.cap = 2, 1, 64, 8, 1000, 1024
+    a.head_dim, a.v_tile_rows, a.num_splits, a.softmax_scale = 128, 256, 0, 0.088
+    a.workspace, a.workspace_bytes = 1 << 20, 1 << 30
+    for k, v in kw.items():
+        if k.endswith("stride"):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_len=9), 2), (dict(kv_len=1025), 2), (dict(kv_len=0), 2), (dict(head_dim=256), 2),
+    (dict(v_tile_rows=16), 2), (dict(num_splits=-1), 2), (dict(v_codes=None), 1),
+    (dict(q_stride=[64 * 128, 64 * 128, 100]), 3), (dict(k_codes=4104), 3), (dict(workspace_bytes=0), 5),
+])
+def test_decode_validation(kw, status):
+    assert ops.lib().qk4v8_attn_decode(ctypes.byref(_decode(**kw)), None) == status
+
+
+def test_decode_workspace_query():
+    L = ops.lib()
+    a = _decode(num_splits=4)
+    # partial outputs: batch * kv_heads * splits * (G * q_len) rows of head_dim fp32 + one lse each
+    rows = 2 * 8 * 4 * 8
+    assert L.qk4v8_decode_workspace_bytes(ctypes.byref(a)) >= rows * (128 * 4 + 4)
+    assert L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(q_len=9))) == 0
