@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of the QK4V8 hot path on one MI355X, printed as ONE JSON line.
+
+Step = one full prefill of the causal GQA workload (batch 4, 32 query / 8 KV
+heads, 4096 tokens, head_dim 128, 4 outlier K channels x20): the K/V quantize
+pre-pass plus the attention kernel, which quantizes Q in its prologue.  The
+decode (batch 64, 64/8 heads, 32768 cached tokens) and block-verify (batch 32,
+8 queries over 16384 + 8 cached tokens) workloads are timed in the same run and
+reported as extra objects.  Inputs are seeded and synthetic and resident in HBM
+before timing starts.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_FP4_TFLOPS = 10100.0      # dense MXFP4 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # dense FP8 MFMA
+# QK^T runs on FP4 and P·V on FP8 with equal algorithmic flops, so the time
+# floor is F/2/P_fp4 + F/2/P_fp8, i.e. the harmonic mean of the two peaks.
+PEAK_MIXED_TFLOPS = 2.0 / (1.0 / PEAK_FP4_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_causal_gqa_n4096_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "bit_quantized_attention_online_amd", "csrc", "prefill.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def causal_pairs(nq, nk):
+    off = nk - nq
+    return sum(min(nk, i + off + 1) for i in range(nq))
+
+
+class Events:
+    """hipEvents recorded on the stream the library launches on."""
+
+    def __init__(self, torch, n):
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def record(self, i, stream):
+        self.ev[i].record(stream)
+
+    def ms(self, i, j):
+        return self.ev[i].elapsed_time(self.ev[j])
+
+
+def bench_prefill(torch, ops, synth, steps, warmup):
+    w = synth.WORKLOADS[2]
+    log("[bench] generating the causal GQA prefill workload")
+    q, k, v = synth.prefill_inputs(2)
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a.view("int16")).to(dev).view(torch.bfloat16)
+    qd, kd, vd = to(q), to(k), to(v)
+    del q, k, v
+    pp = ops.PackedPrefill(qd, kd, vd, causal=True, softmax_scale=1.0 / math.sqrt(w["d"]),
+                           v_tile_rows=w["v_tile_rows"])
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        pp.pack()
+        pp.attend()
+    torch.cuda.synchronize()
+    evs = [Events(torch, 3) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e.record(0, stream)
+        pp.pack(stream)
+        e.record(1, stream)
+        pp.attend(stream)
+        e.record(2, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pack_ms = sum(e.ms(0, 1) for e in evs) / steps
+    attn_ms = sum(e.ms(1, 2) for e in evs) / steps
+    assert torch.isfinite(pp.o.float()).all().item(), "non-finite prefill output"
+    pairs = w["B"] * w["Hq"] * causal_pairs(w["Nq"], w["Nk"])
+    flops = pairs * 4.0 * w["d"]
+    return dict(w=w, wall_ms=wall * 1e3 / steps, pack_ms=pack_ms, attn_ms=attn_ms, flops=flops, pairs=pairs)
+
+
+def build_cache(torch, ops, w, seed):
+    """Quantized K/V cache of a decode workload, drawn on the GPU with torch's
+    seeded generator (N(0,1) -> bf16) and quantized by the library."""
+    B, Hkv, n, d, R = w["B"], w["Hkv"], w["kv_len"], w["d"], w["v_tile_rows"]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    kc = torch.empty((B, Hkv, n, d // 2), dtype=torch.uint8, device=dev)
+    ks = torch.empty((B, Hkv, n, d // 32), dtype=torch.uint8, device=dev)
+    vc = torch.empty((B, Hkv, n, d), dtype=torch.uint8, device=dev)
+    vs = torch.empty((B, Hkv, -(-n // R)), dtype=torch.uint8, device=dev)
+    for b in range(B):
+        kb = torch.randn((Hkv, n, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vb = torch.randn((Hkv, n, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        c, s = ops.quantize_qk(kb)
+        kc[b].copy_(c)
+        ks[b].copy_(s)
+        c, s = ops.quantize_v(vb, R)
+        vc[b].copy_(c)
+        vs[b].copy_(s)
+    q = torch.randn((B, w["q_len"], w["Hq"], d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    return q, kc, ks, vc, vs
+
+
+def bench_decode(torch, ops, synth, cfg, steps, warmup):
+    w = synth.WORKLOADS[cfg]
+    log(f"[bench] building the quantized cache of workload {w['name']}")
+    q, kc, ks, vc, vs = build_cache(torch, ops, w, seed=1000 + cfg)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    ws = torch.empty(max(1, ops.decode_workspace_bytes(q, kc, w["kv_len"], w["v_tile_rows"])), dtype=torch.uint8,
+                     device=q.device)
+    run = lambda: ops.attn_decode(q, kc, ks, vc, vs, w["kv_len"], v_tile_rows=w["v_tile_rows"], out=o, workspace=ws,
+                                  softmax_scale=1.0 / math.sqrt(w["d"]))
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [Events(torch, 2) for _ in range(steps)]
+    for e in evs:
+        e.record(0, stream)
+        run()
+        e.record(1, stream)
+    torch.cuda.synchronize()
+    ms = sum(e.ms(0, 1) for e in evs) / steps
+    assert torch.isfinite(o.float()).all().item(), "non-finite decode output"
+    d = w["d"]
+    per_token = d // 2 + d // 32 + d                       # K codes + K scales + V codes per kv-head
+    kv_bytes = w["B"] * w["Hkv"] * (w["kv_len"] * per_token + -(-w["kv_len"] // w["v_tile_rows"]))
+    qo_bytes = 2 * (w["B"] * w["q_len"] * w["Hq"] * d * 2)
+    gbs = (kv_bytes + qo_bytes) / (ms * 1e-3) / 1e9
+    del kc, ks, vc, vs
+    return dict(workload=w["name"], value=round(gbs, 1), unit="GB/s", ms=round(ms, 4),
+                bytes=kv_bytes + qo_bytes,
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+
+
+def cpu_baseline(synth):
+    """The oracle as it stands, on a bounded sample of the prefill workload:
+    batch 0 (all 32 query heads / 8 KV heads, all 4096 positions), about a
+    quarter of the step."""
+    import numpy as np
+    from oracle import attention as oatt
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    w = synth.WORKLOADS[2]
+    q, k, v = synth.prefill_inputs(2)
+    G = w["Hq"] // w["Hkv"]
+    kvh = w["Hkv"]
+    qs, ks_, vs_ = q[:1, :kvh * G], k[:1, :kvh], v[:1, :kvh]
+    t0 = time.perf_counter()
+    o, _ = oatt.qk4v8_prefill(qs, ks_, vs_, 1.0 / math.sqrt(w["d"]), True, w["v_tile_rows"])
+    dt = time.perf_counter() - t0
+    assert np.isfinite(o).all()
+    flops = kvh * G * causal_pairs(w["Nq"], w["Nk"]) * 4.0 * w["d"]
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"batch 0, query heads 0-{kvh * G - 1} (KV heads 0-{kvh - 1}) of the causal GQA prefill, "
+                       f"all {w['Nq']} positions: {dt:.1f} s of numpy fp64 including the quantizers")
+
+
+def calib_copy(torch, nbytes=1 << 30):
+    """A plain device copy of known size, run once so that the same rocprofv3
+    --pmc run records FETCH_SIZE / WRITE_SIZE for it (counter scale factor)."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the QK4V8 path here has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from bit_quantized_attention_online_amd import ops, synth
+    ops.lib()
+    if args.calib_copy:
+        calib_copy(torch)
+
+    pf = bench_prefill(torch, ops, synth, args.steps, args.warmup)
+    step_ms = pf["pack_ms"] + pf["attn_ms"]
+    value = pf["flops"] / (step_ms * 1e-3) / 1e12
+    attn_tflops = pf["flops"] / (pf["attn_ms"] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("source_sha256_16") == source_hash(ATTN_SOURCE):
+            traffic = t.get("bytes_per_launch")
+    line = {
+        "metric": "QK4V8 attn: prefill TFLOP/s + decode KV GB/s, % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4xmxfp4+fp8xfp8->fp32",
+        "data": "synthetic",
+        "config": {"workload": pf["w"]["name"], "batch": pf["w"]["B"], "q_heads": pf["w"]["Hq"],
+                   "kv_heads": pf["w"]["Hkv"], "seq_len": pf["w"]["Nq"], "head_dim": pf["w"]["d"],
+                   "causal": True, "v_tile_rows": pf["w"]["v_tile_rows"],
+                   "algorithmic_flops": pf["flops"]},
+        "wall_ms_per_step": round(pf["wall_ms"], 4),
+        "prefill_breakdown_ms": {"pack_kv": round(pf["pack_ms"], 4), "attention": round(pf["attn_ms"], 4)},
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel<128,causal>",
+                     "achieved": round(attn_tflops, 1), "peak": round(PEAK_MIXED_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_MIXED_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.skip_decode:
+        line["decode"] = bench_decode(torch, ops, synth, 3, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        line["block_verify"] = bench_decode(torch, ops, synth, 5, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        line["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

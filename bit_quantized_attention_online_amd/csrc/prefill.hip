@@ -471,26 +471,29 @@ static int gcd_int(int x, int y) {
 }
 
 template <int D>
-static hipError_t launch_prefill_d(const PrefillParams& p, hipStream_t stream) {
+static hipError_t launch_pack_d(const PrefillParams& p, hipStream_t stream) {
   const PrefillLayout L = prefill_layout(p.batch, p.kv_heads, p.seq_k, D, p.v_tile_rows);
-  uint8_t* wk = p.ws + L.off_k;
-  uint8_t* wks = p.ws + L.off_ks;
-  uint8_t* wv = p.ws + L.off_v;
-  uint32_t* wvs = reinterpret_cast<uint32_t*>(p.ws + L.off_vs);
   uint8_t* wvt = p.ws + L.off_vtile;
   const int64_t bk = (int64_t)p.batch * p.kv_heads;
-
   const int64_t total_k = bk * L.n_tiles * kKvTile * (D / 32);
   hipLaunchKernelGGL((pack_k_kernel<D>), dim3((unsigned)((total_k + 255) / 256)), dim3(256), 0, stream, p.k,
-                     p.ks[0], p.ks[1], p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, wk, wks, total_k);
+                     p.ks[0], p.ks[1], p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, p.ws + L.off_k, p.ws + L.off_ks,
+                     total_k);
   hipLaunchKernelGGL((vtile_scale_kernel<D>), dim3((unsigned)(bk * L.n_vtiles)), dim3(256), 0, stream, p.v,
                      p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_vtiles, wvt);
   hipLaunchKernelGGL((pack_v_kernel<D>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v, p.vs[0],
-                     p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_tiles, L.n_vtiles, wvt, wv, wvs);
+                     p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_tiles, L.n_vtiles, wvt,
+                     p.ws + L.off_v, reinterpret_cast<uint32_t*>(p.ws + L.off_vs));
+  return hipGetLastError();
+}
 
+template <int D>
+static hipError_t launch_attn_d(const PrefillParams& p, hipStream_t stream) {
+  const PrefillLayout L = prefill_layout(p.batch, p.kv_heads, p.seq_k, D, p.v_tile_rows);
   AttnArgs a;
   a.q = p.q; a.o = p.o; a.lse = p.lse;
-  a.wk = wk; a.wks = wks; a.wv = wv; a.wvs = wvs;
+  a.wk = p.ws + L.off_k; a.wks = p.ws + L.off_ks; a.wv = p.ws + L.off_v;
+  a.wvs = reinterpret_cast<const uint32_t*>(p.ws + L.off_vs);
   a.qs0 = p.qs[0]; a.qs1 = p.qs[1]; a.qs2 = p.qs[2];
   a.os0 = p.os[0]; a.os1 = p.os[1]; a.os2 = p.os[2];
   a.q_heads = p.q_heads; a.kv_heads = p.kv_heads;
@@ -511,8 +514,12 @@ static hipError_t launch_prefill_d(const PrefillParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  return p.head_dim == 64 ? launch_prefill_d<64>(p, stream) : launch_prefill_d<128>(p, stream);
+hipError_t launch_prefill_pack(const PrefillParams& p, hipStream_t stream) {
+  return p.head_dim == 64 ? launch_pack_d<64>(p, stream) : launch_pack_d<128>(p, stream);
+}
+
+hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t stream) {
+  return p.head_dim == 64 ? launch_attn_d<64>(p, stream) : launch_attn_d<128>(p, stream);
 }
 
 }  // namespace qk4v8

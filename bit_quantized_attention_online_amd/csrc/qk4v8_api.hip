@@ -160,7 +160,13 @@ size_t qk4v8_prefill_workspace_bytes(const qk4v8_prefill_args* a) {
   return prefill_layout(a->batch, a->kv_heads, a->seq_k, a->head_dim, a->v_tile_rows).total;
 }
 
-qk4v8_status qk4v8_attn_prefill(const qk4v8_prefill_args* a, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+enum PrefillPart { kPack = 1, kAttn = 2 };
+
+qk4v8_status run_prefill(const qk4v8_prefill_args* a, hipStream_t stream, int parts) {
   qk4v8_status st = validate_prefill(a);
   if (st != QK4V8_OK) return st;
   if (a->batch == 0 || a->seq_q == 0) return QK4V8_OK;
@@ -177,7 +183,28 @@ qk4v8_status qk4v8_attn_prefill(const qk4v8_prefill_args* a, hipStream_t stream)
   p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows; p.causal = a->causal;
   p.softmax_scale = a->softmax_scale;
   p.ws = static_cast<uint8_t*>(a->workspace);
-  return from_hip(launch_prefill(p, stream));
+  if (parts & kPack) {
+    st = from_hip(launch_prefill_pack(p, stream));
+    if (st != QK4V8_OK) return st;
+  }
+  if (parts & kAttn) st = from_hip(launch_prefill_attn(p, stream));
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+qk4v8_status qk4v8_attn_prefill(const qk4v8_prefill_args* a, hipStream_t stream) {
+  return run_prefill(a, stream, kPack | kAttn);
+}
+
+qk4v8_status qk4v8_prefill_pack_kv(const qk4v8_prefill_args* a, hipStream_t stream) {
+  return run_prefill(a, stream, kPack);
+}
+
+qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t stream) {
+  return run_prefill(a, stream, kAttn);
 }
 
 size_t qk4v8_decode_workspace_bytes(const qk4v8_decode_args* a) {

@@ -35,7 +35,8 @@ struct PrefillParams {
   float softmax_scale;
   uint8_t* ws;
 };
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill_pack(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t stream);
 
 struct DecodeParams {
   const uint16_t* q;

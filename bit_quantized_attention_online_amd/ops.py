@@ -19,8 +19,8 @@ STATUS_NAMES = {0: "QK4V8_OK", 1: "QK4V8_ERR_NULL", 2: "QK4V8_ERR_SHAPE", 3: "QK
                 4: "QK4V8_ERR_UNSUPPORTED", 5: "QK4V8_ERR_WORKSPACE", 6: "QK4V8_ERR_HIP"}
 
 EXPORTED = ["qk4v8_abi_version", "qk4v8_status_string", "qk4v8_quantize_qk", "qk4v8_quantize_v",
-            "qk4v8_prefill_workspace_bytes", "qk4v8_attn_prefill", "qk4v8_decode_workspace_bytes",
-            "qk4v8_attn_decode"]
+            "qk4v8_prefill_workspace_bytes", "qk4v8_attn_prefill", "qk4v8_prefill_pack_kv",
+            "qk4v8_attn_prefill_packed", "qk4v8_decode_workspace_bytes", "qk4v8_attn_decode"]
 
 
 class PrefillArgs(ctypes.Structure):
@@ -73,8 +73,9 @@ def lib():
                                        ctypes.c_void_p, ctypes.c_void_p]
         L.qk4v8_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.qk4v8_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
-        L.qk4v8_attn_prefill.restype = ctypes.c_int
-        L.qk4v8_attn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), ctypes.c_void_p]
+        for fn in ("qk4v8_attn_prefill", "qk4v8_prefill_pack_kv", "qk4v8_attn_prefill_packed"):
+            getattr(L, fn).restype = ctypes.c_int
+            getattr(L, fn).argtypes = [ctypes.POINTER(PrefillArgs), ctypes.c_void_p]
         L.qk4v8_decode_workspace_bytes.restype = ctypes.c_size_t
         L.qk4v8_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
         L.qk4v8_attn_decode.restype = ctypes.c_int
@@ -173,6 +174,31 @@ def attn_prefill(q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, retu
     a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _check(lib().qk4v8_attn_prefill(ctypes.byref(a), _stream(stream)), "qk4v8_attn_prefill")
     return (o, lse) if return_lse else o
+
+
+class PackedPrefill:
+    """A prefill split in its two library calls with one reusable workspace:
+    ``pack()`` quantizes K/V into the workspace, ``attend()`` runs the
+    attention kernel from it (used to time the two halves separately)."""
+
+    def __init__(self, q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False):
+        for t in (q, k, v):
+            _bits16(t)
+        self.o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+        self.args = _prefill_args(q, k, v, self.o, self.lse, causal, softmax_scale, v_tile_rows)
+        need = lib().qk4v8_prefill_workspace_bytes(ctypes.byref(self.args))
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        self.args.workspace, self.args.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
+        self._keep = (q, k, v)
+
+    def pack(self, stream=None):
+        _check(lib().qk4v8_prefill_pack_kv(ctypes.byref(self.args), _stream(stream)), "qk4v8_prefill_pack_kv")
+
+    def attend(self, stream=None):
+        _check(lib().qk4v8_attn_prefill_packed(ctypes.byref(self.args), _stream(stream)),
+               "qk4v8_attn_prefill_packed")
+        return self.o
 
 
 def _decode_args(q, k_codes, k_scales, v_codes, v_scales, o, lse, kv_len, v_tile_rows, kv_lens, num_splits,

@@ -149,6 +149,20 @@ size_t qk4v8_prefill_workspace_bytes(const qk4v8_prefill_args* a);
 qk4v8_status qk4v8_attn_prefill(const qk4v8_prefill_args* a, hipStream_t stream);
 
 /*
+ * The two halves of qk4v8_attn_prefill, for callers that reuse one quantized
+ * K/V for several query chunks, or time the attention kernel alone:
+ *   qk4v8_prefill_pack_kv      quantizes K (MXFP4) and V (per-tile FP8) into the
+ *                              workspace; reads k, v; ignores q, o and lse.
+ *   qk4v8_attn_prefill_packed  runs the attention from a workspace filled by a
+ *                              pack call with the same batch, kv_heads, seq_k,
+ *                              head_dim and v_tile_rows; reads q, writes o and
+ *                              lse; ignores k and v.
+ * Validation and status codes are those of qk4v8_attn_prefill.
+ */
+qk4v8_status qk4v8_prefill_pack_kv(const qk4v8_prefill_args* a, hipStream_t stream);
+qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t stream);
+
+/*
  * Decode / block-verify attention over a quantized KV cache (MpFA page §1.3:
  * decode is memory-bound and 4-bit K cuts its traffic; §6.1: combined with a
  * quantized KV cache).  q_len new query tokens per sequence (1 for decode, or a
