@@ -24,7 +24,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazyRescale = 8.0f;
 
 __host__ __device__ constexpr int subtile_key(int t, int r) {
   return (t >> 2) * 64 + 16 * (r >> 2) + 4 * (t & 3) + (r & 3);
@@ -92,7 +91,7 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
   const int qt = row_ok ? mrow / a.group : 0;
   const int head = kvh * a.group + (row_ok ? mrow - qt * a.group : 0);
   const int lim = row_ok ? kvlen - a.q_len + qt : -1;   // last visible key
-  v8i qf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  uint4 qc = make_uint4(0, 0, 0, 0);
   int qsc = 127;
   if (row_ok && lg < NB) {
     const uint4* src = reinterpret_cast<const uint4*>(a.q + b * a.qs0 + qt * a.qs1 + (int64_t)head * a.qs2 + 32 * lg);
@@ -104,93 +103,94 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
     }
     uint32_t cq[4];
     qsc = (int)mxfp4_quantize32(w, cq);
-    qf[0] = (int)cq[0]; qf[1] = (int)cq[1]; qf[2] = (int)cq[2]; qf[3] = (int)cq[3];
+    qc = make_uint4(cq[0], cq[1], cq[2], cq[3]);
   }
+  const v8i qf = fp4_operand(qc);
 
   v4f O[ND];
 #pragma unroll
   for (int dd = 0; dd < ND; ++dd) O[dd] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
+  v4f L = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  v8i Phi = v8i{}, Plo = v8i{};
+  const v8i ones = v8i{(int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones,
+                       (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones};
+  const int klg = lg & (NB - 1);    // D = 64: lanes of k-blocks 2, 3 reread blocks 0, 1 (their Q is zero)
 
   const uint8_t* gk = a.kc + bk * (int64_t)a.cap * (D / 2);
   const uint32_t* gks = reinterpret_cast<const uint32_t*>(a.ksc + bk * (int64_t)a.cap * NB);
   const uint8_t* gv = a.vc + bk * (int64_t)a.cap * D;
   const uint8_t* gvs = a.vsc + bk * a.n_vtiles_cap;
 
-  // ---- tile staging (registers hold the next tile while this one computes) ----
+  // ---- tile staging: the next tile is held in registers while this one
+  // computes, then written to LDS (K rows padded, V chunks XOR-swizzled) ----
   constexpr int KCH = 128 * NB;          // 16-byte K chunks per tile
   constexpr int VCH = 128 * NC;          // 16-byte V chunks per tile
   constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VCH + NT - 1) / NT, SPT = (128 + NT - 1) / NT;
-  uint4 rk[KPT], rv[VPT];
+  v4i rk[KPT], rv[VPT];   // clang vectors (not HIP's uint4 struct) so SROA keeps them in VGPRs
   uint32_t rs[SPT];
-  auto gload = [&](int tile) {
-    const int j0 = j_begin + tile * 128;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
+  // all accesses to rk / rv / rs use compile-time indices (static_for) so the
+  // arrays stay in registers
+  auto dload = [&](int tile) __attribute__((always_inline)) {
+    const int j0_ = j_begin + tile * 128;
+    static_for<KPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
       const int ci = tid + i * NT;
-      if (ci < KCH) {
-        const int key = min(j0 + ci / NB, a.cap - 1);
-        rk[i] = *reinterpret_cast<const uint4*>(gk + (int64_t)key * (D / 2) + (ci % NB) * 16);
+      if (KCH % NT == 0 || ci < KCH) {
+        const int key = min(j0_ + ci / NB, a.cap - 1);
+        rk[i] = *reinterpret_cast<const v4i*>(gk + (int64_t)key * (D / 2) + (ci % NB) * 16);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
+    });
+    static_for<VPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
       const int ci = tid + i * NT;
-      if (ci < VCH) {
-        const int key = min(j0 + ci / NC, a.cap - 1);
-        rv[i] = *reinterpret_cast<const uint4*>(gv + (int64_t)key * D + (ci % NC) * 16);
+      if (VCH % NT == 0 || ci < VCH) {
+        const int key = min(j0_ + ci / NC, a.cap - 1);
+        rv[i] = *reinterpret_cast<const v4i*>(gv + (int64_t)key * D + (ci % NC) * 16);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
+    });
+    static_for<SPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
       const int ki = tid + i * NT;
-      if (ki < 128) {
-        const int key = min(j0 + ki, a.cap - 1);
+      if (128 % NT == 0 || ki < 128) {
+        const int key = min(j0_ + ki, a.cap - 1);
         rs[i] = NB == 4 ? gks[key] : (uint32_t)reinterpret_cast<const uint16_t*>(gks)[key];
       }
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ci = tid + i * NT;
-      if (ci < KCH) *reinterpret_cast<uint4*>(lk + (ci / NB) * T::KRB + (ci % NB) * 16) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int ci = tid + i * NT;
-      if (ci < VCH) {
-        const int row = ci / NC;
-        *reinterpret_cast<uint4*>(lv + row * D + vswz<D>(row, ci % NC) * 16) = rv[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int ki = tid + i * NT;
-      if (ki < 128) reinterpret_cast<uint32_t*>(lks)[ki] = rs[i];
-    }
+    });
   };
 
-  if (ntiles > 0) gload(0);
+  if (ntiles > 0) dload(0);
   for (int it = 0; it < ntiles; ++it) {
     const int j0 = j_begin + it * 128;
     __syncthreads();            // previous tile fully consumed
-    sstore();
+    static_for<KPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int ci = tid + i * NT;
+      if (KCH % NT == 0 || ci < KCH) *reinterpret_cast<v4i*>(lk + (ci / NB) * T::KRB + (ci % NB) * 16) = rk[i];
+    });
+    static_for<VPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int ci = tid + i * NT;
+      if (VCH % NT == 0 || ci < VCH) {
+        const int row = ci / NC;
+        *reinterpret_cast<v4i*>(lv + row * D + vswz<D>(row, ci % NC) * 16) = rv[i];
+      }
+    });
+    static_for<SPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int ki = tid + i * NT;
+      if (128 % NT == 0 || ki < 128) reinterpret_cast<uint32_t*>(lks)[ki] = rs[i];
+    });
     __syncthreads();            // this tile visible
-    if (it + 1 < ntiles) gload(it + 1);
+    if (it + 1 < ntiles) dload(it + 1);
 
     // ---- S^T = K · Q^T ----
     v4f S[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int key = subtile_key(t, ql);
-      v8i af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      int sa = 127;
-      if (lg < NB) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(lk + key * T::KRB + lg * 16);
-        af[0] = (int)kv.x; af[1] = (int)kv.y; af[2] = (int)kv.z; af[3] = (int)kv.w;
-        sa = (int)((reinterpret_cast<const uint32_t*>(lks)[key] >> (8 * lg)) & 0xFF);
-      }
+      const v8i af = fp4_operand(*reinterpret_cast<const uint4*>(lk + key * T::KRB + klg * 16));
+      const int sa = (int)((reinterpret_cast<const uint32_t*>(lks)[key] >> (8 * klg)) & 0xFF);
       S[t] = mfma16x16x128<kFmtFp4, kFmtFp4>(af, qf, v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc);
     }
     // ---- mask: keys past this row's limit (covers kv_len and the causal block) ----
@@ -202,42 +202,9 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
           if (j0 + subtile_key(t, 4 * lg + i) > lim) S[t][i] = -INFINITY;
     }
     // ---- online softmax + two-term FP8 P ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float tmax = mx * a.c;
-    const float m_new = fmaxf(m_run, tmax);
-    if (__any(m_new > m_run + kLazyRescale)) {
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int dd = 0; dd < ND; ++dd) O[dd] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
-    const float sh = exp2i(X), sl = exp2i(X - 4);
-    v8i Phi, Plo;
-    float lsum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(S[t][i], a.c, -m_use));
-      lsum += (p[0] + p[1]) + (p[2] + p[3]);
-      const uint32_t h01 = e4m3_pack2(p[0], p[1], sh);
-      const uint32_t h23 = e4m3_pack2(p[2], p[3], sh);
-      const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h01, sh, false);
-      const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h23, sh, false);
-      const uint32_t l01 = e4m3_pack2(p[0] - b01[0], p[1] - b01[1], sl);
-      const uint32_t l23 = e4m3_pack2(p[2] - b23[0], p[3] - b23[1], sl);
-      Phi[t] = (int)(h01 | (h23 << 16));
-      Plo[t] = (int)(l01 | (l23 << 16));
-    }
-    l_part += lsum;
-    // ---- O^T += V^T · P^T ----
+    int psc;
+    softmax_tile<ND>(S, a.c, m_run, O, L, Phi, Plo, psc);
+    // ---- O^T += V^T · P^T, L += 1 · P^T ----
     const int vkey = min(j0 + 32 * lg, a.cap - 1);
     const int vs = (int)gvs[vkey / a.R];
     const int src_row_in_piece = ql >> 1, src_half = ql & 1;
@@ -252,16 +219,16 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
         av[2 * pc] = r[0];
         av[2 * pc + 1] = r[1];
       }
-      O[dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(av, Phi, O[dd], vs, X + 127);
-      O[dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(av, Plo, O[dd], vs, X + 123);
+      O[dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(av, Phi, O[dd], vs, psc);
+      O[dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(av, Plo, O[dd], vs, psc - 4);
     }
+    L = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Phi, L, 127, psc);
+    L = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Plo, L, 127, psc - 4);
   }
 
   // ---- write this split's normalized partial and its log2-sum-exp ----
-  float l = l_part;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
   if (!row_ok) return;
+  const float l = L[0];
   const int64_t prow = (bk * a.splits + s) * a.M + mrow;
   const bool empty = !(l > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l;

@@ -35,7 +35,6 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;          // two 16-row query blocks
-constexpr float kLazyRescale = 8.0f;      // log2 headroom before rescaling O
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -275,12 +274,14 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
   const uint8_t* gv = a.wv + bk * a.n_tiles * TB::V;
   const uint32_t* gvs = a.wvs + bk * a.n_tiles;
 
-  // ---- Q prologue: quantize this wave's 32 rows to MXFP4 in registers ----
+  // ---- Q prologue: quantize this wave's 32 rows to MXFP4 in registers.
+  // Lanes of k-blocks past head_dim (D = 64) hold zero codes, so whatever K
+  // codes those lanes read contribute nothing.
   v8i qf[2];
   int qsc[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    qf[qb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    uint4 qc = make_uint4(0, 0, 0, 0);
     qsc[qb] = 127;
     const int row = p0w + qb * 16 + ql;
     if (row < a.seq_q && lg < NB) {
@@ -293,50 +294,59 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
       }
       uint32_t c[4];
       qsc[qb] = (int)mxfp4_quantize32(w, c);
-      qf[qb][0] = (int)c[0]; qf[qb][1] = (int)c[1]; qf[qb][2] = (int)c[2]; qf[qb][3] = (int)c[3];
+      qc = make_uint4(c[0], c[1], c[2], c[3]);
     }
+    qf[qb] = fp4_operand(qc);
   }
 
   v4f O[2][ND];
+  v4f L[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < 2; ++qb) {
+    L[qb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dd = 0; dd < ND; ++dd) O[qb][dd] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
   float m_run[2] = {-INFINITY, -INFINITY};
-  float l_part[2] = {0.f, 0.f};
+  v8i Phi[2] = {v8i{}, v8i{}}, Plo[2] = {v8i{}, v8i{}};
+  const v8i ones = v8i{(int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones,
+                       (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones};
+  const int klane = lane & (NB * 16 - 1);   // K fragment lane (D = 64 reuses lanes 0..31)
 
-  // ---- tile staging: global -> registers -> LDS ----
+  // ---- tile staging: global -> registers -> LDS (double-buffered LDS) ----
   constexpr int KV4 = TB::K / 16, VV4 = TB::V / 16, KSV4 = TB::KS / 16;
   uint4 rk = make_uint4(0, 0, 0, 0), rv0 = rk, rv1 = rk, rks = rk;
   uint32_t rvs = 0;
-  auto gload = [&](int tile) {
-    const uint4* sk = reinterpret_cast<const uint4*>(gk + (int64_t)tile * TB::K);
-    const uint4* sv = reinterpret_cast<const uint4*>(gv + (int64_t)tile * TB::V);
-    const uint4* sks = reinterpret_cast<const uint4*>(gks + (int64_t)tile * TB::KS);
-    if (tid < KV4) rk = sk[tid];
-    if (tid < VV4) rv0 = sv[tid];
-    if (tid + kThreads < VV4) rv1 = sv[tid + kThreads];
-    if (tid < KSV4) rks = sks[tid];
-    if (tid == 0) rvs = gvs[tile];
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* base = lds + buf * TB::STAGE;
-    if (tid < KV4) reinterpret_cast<uint4*>(base)[tid] = rk;
-    if (tid < VV4) reinterpret_cast<uint4*>(base + TB::K + TB::KS)[tid] = rv0;
-    if (tid + kThreads < VV4) reinterpret_cast<uint4*>(base + TB::K + TB::KS)[tid + kThreads] = rv1;
-    if (tid < KSV4) reinterpret_cast<uint4*>(base + TB::K)[tid] = rks;
-    if (tid == 0) *reinterpret_cast<uint32_t*>(base + TB::K + TB::KS + TB::V) = rvs;
-  };
+#define QK4V8_GLOAD(tile)                                                                    \
+  do {                                                                                       \
+    const uint4* sk_ = reinterpret_cast<const uint4*>(gk + (int64_t)(tile) * TB::K);        \
+    const uint4* sv_ = reinterpret_cast<const uint4*>(gv + (int64_t)(tile) * TB::V);        \
+    const uint4* sks_ = reinterpret_cast<const uint4*>(gks + (int64_t)(tile) * TB::KS);     \
+    if (tid < KV4) rk = sk_[tid];                                                            \
+    if (tid < VV4) rv0 = sv_[tid];                                                           \
+    if (tid + kThreads < VV4) rv1 = sv_[tid + kThreads];                                     \
+    if (tid < KSV4) rks = sks_[tid];                                                         \
+    if (tid == 0) rvs = gvs[(tile)];                                                         \
+  } while (0)
+#define QK4V8_SSTORE(buf)                                                                    \
+  do {                                                                                       \
+    uint8_t* base_ = lds + (buf) * TB::STAGE;                                                \
+    if (tid < KV4) reinterpret_cast<uint4*>(base_)[tid] = rk;                                \
+    if (tid < VV4) reinterpret_cast<uint4*>(base_ + TB::K + TB::KS)[tid] = rv0;              \
+    if (tid + kThreads < VV4) reinterpret_cast<uint4*>(base_ + TB::K + TB::KS)[tid + kThreads] = rv1; \
+    if (tid < KSV4) reinterpret_cast<uint4*>(base_ + TB::K)[tid] = rks;                      \
+    if (tid == 0) *reinterpret_cast<uint32_t*>(base_ + TB::K + TB::KS + TB::V) = rvs;        \
+  } while (0)
 
   if (nt_wg > 0) {
-    gload(0);
-    sstore(0);
+    QK4V8_GLOAD(0);
+    QK4V8_SSTORE(0);
   }
   __syncthreads();
 
   for (int j = 0; j < nt_wg; ++j) {
     const int buf = j & 1;
-    if (j + 1 < nt_wg) gload(j + 1);
+    if (j + 1 < nt_wg) QK4V8_GLOAD(j + 1);
     if (j < nt_w) {
       const uint8_t* base = lds + buf * TB::STAGE;
       const uint8_t* lk = base;
@@ -344,85 +354,39 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
       const uint8_t* lv = base + TB::K + TB::KS;
       const uint32_t vsw = *reinterpret_cast<const uint32_t*>(base + TB::K + TB::KS + TB::V);
 
-      // ---- S^T = K · Q^T  (FP4 x FP4, scales applied in the MFMA) ----
+      // ---- S^T = K · Q^T  (FP4 x FP4; both operands' E8M0 scales applied
+      // inside the instruction, i.e. the scores come out dequantized) ----
       v4f S[2][8];
-      uint2 ksc = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-      if (lg < NB) ksc = *reinterpret_cast<const uint2*>(lks + lane * 8);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        v8i af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        if (lg < NB) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(lk + (t * NB * 16 + lane) * 16);
-          af[0] = (int)kv.x; af[1] = (int)kv.y; af[2] = (int)kv.z; af[3] = (int)kv.w;
-        }
-        const int sa = (int)(((t < 4 ? ksc.x : ksc.y) >> (8 * (t & 3))) & 0xFF);
+      const uint2 ksc = *reinterpret_cast<const uint2*>(lks + klane * 8);
+      static_for<8>([&](auto T) {
+        constexpr int t = decltype(T)::value;
+        const v8i af = fp4_operand(*reinterpret_cast<const uint4*>(lk + (t * NB * 16 + klane) * 16));
+        const int sa = (int)(t < 4 ? ksc.x : ksc.y);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          S[qb][t] = mfma16x16x128<kFmtFp4, kFmtFp4>(af, qf[qb], v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc[qb]);
-      }
+          S[qb][t] = mfma16x16x128<kFmtFp4, kFmtFp4, t & 3, 0>(af, qf[qb], v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc[qb]);
+      });
 
       // ---- mask (only tiles that cross the causal diagonal or seq_k) ----
       if (j * kKvTile + kKvTile - 1 > mask_lim) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int row = p0w + qb * 16 + ql;
-          const int lim = CAUSAL ? min(a.seq_k - 1, row + off) : a.seq_k - 1;
+          const int lim = (CAUSAL ? min(a.seq_k - 1, row + off) : a.seq_k - 1) - j * kKvTile;
 #pragma unroll
           for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = j * kKvTile + subtile_key(t, 4 * lg + i);
-              if (key > lim) S[qb][t][i] = -INFINITY;
-            }
+            for (int i = 0; i < 4; ++i)
+              if (subtile_key(t, 4 * lg + i) > lim) S[qb][t][i] = -INFINITY;
         }
       }
 
-      // ---- online softmax (log2 domain) and two-term FP8 P ----
-      v8i Phi[2], Plo[2];
+      // ---- online softmax and two-term FP8 P ----
       int psc[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          mx = fmaxf(mx, fmaxf(fmaxf(S[qb][t][0], S[qb][t][1]), fmaxf(S[qb][t][2], S[qb][t][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float tmax = mx * a.c;
-        const float m_new = fmaxf(m_run[qb], tmax);
-        if (__any(m_new > m_run[qb] + kLazyRescale)) {
-          const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-          l_part[qb] *= alpha;
-#pragma unroll
-          for (int dd = 0; dd < ND; ++dd) O[qb][dd] *= alpha;
-          m_run[qb] = m_new;
-        }
-        const float m_use = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-        // per-(row, tile) range scale: the tile's largest p is 2^(tmax - m)
-        const float dl = fmaxf(tmax - m_use, -100.0f);
-        const int X = (int)floorf(dl) - 7;
-        psc[qb] = X + 127;
-        const float sh = exp2i(X), sl = exp2i(X - 4);
-        float lsum = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          float p[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(S[qb][t][i], a.c, -m_use));
-          lsum += (p[0] + p[1]) + (p[2] + p[3]);
-          const uint32_t h01 = e4m3_pack2(p[0], p[1], sh);
-          const uint32_t h23 = e4m3_pack2(p[2], p[3], sh);
-          const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h01, sh, false);
-          const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h23, sh, false);
-          const uint32_t l01 = e4m3_pack2(p[0] - b01[0], p[1] - b01[1], sl);
-          const uint32_t l23 = e4m3_pack2(p[2] - b23[0], p[3] - b23[1], sl);
-          Phi[qb][t] = (int)(h01 | (h23 << 16));
-          Plo[qb][t] = (int)(l01 | (l23 << 16));
-        }
-        l_part[qb] += lsum;
-      }
+      for (int qb = 0; qb < 2; ++qb) softmax_tile<ND>(S[qb], a.c, m_run[qb], O[qb], L[qb], Phi[qb], Plo[qb], psc[qb]);
 
-      // ---- O^T += V^T · P^T  (FP8 x FP8, V tile scale x P range scale) ----
+      // ---- O^T += V^T · P^T and L += 1 · P^T  (FP8 x FP8) ----
       const int vsc = (int)((vsw >> (8 * lg)) & 0xFF);
 #pragma unroll
       for (int dd = 0; dd < ND; ++dd) {
@@ -435,18 +399,24 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
           O[qb][dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(av, Plo[qb], O[qb][dd], vsc, psc[qb] - 4);
         }
       }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        L[qb] = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Phi[qb], L[qb], 127, psc[qb]);
+        L[qb] = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Plo[qb], L[qb], 127, psc[qb] - 4);
+      }
     }
-    if (j + 1 < nt_wg) sstore(buf ^ 1);
+    if (j + 1 < nt_wg) QK4V8_SSTORE(buf ^ 1);
     __syncthreads();
   }
+#undef QK4V8_GLOAD
+#undef QK4V8_SSTORE
 
-  // ---- epilogue: normalize, store bf16 rows and the log-sum-exp ----
+  // ---- epilogue: normalize by the sum of the quantized weights, store bf16
+  // rows and the log-sum-exp ----
   if (!wave_live) return;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float l = l_part[qb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = L[qb][0];     // every row of the ones-MFMA holds the same sum
     const int row = p0w + qb * 16 + ql;
     if (row >= a.seq_q) continue;
     const float inv = 1.0f / l;

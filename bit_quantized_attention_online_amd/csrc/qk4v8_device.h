@@ -23,11 +23,32 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace qk4v8 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v2s __attribute__((ext_vector_type(2)));
+
+// Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(<N-1>), so the
+// index can feed instruction immediates (e.g. the MFMA scale byte select).
+template <int... I, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+// An FP4 MFMA operand: 16 bytes of E2M1 codes in the low half of the 8-dword
+// operand; the upper half is left undefined so the backend passes 4 VGPRs.
+__device__ __forceinline__ v8i fp4_operand(uint4 x) {
+  const v4i v = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+  return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+}
 
 constexpr int kFmtFp8 = 0;   // E4M3 operand format code of the scaled MFMA
 constexpr int kFmtFp4 = 4;   // E2M1 operand format code
@@ -90,6 +111,76 @@ __device__ __forceinline__ uint32_t mxfp4_quantize32(const uint32_t (&w)[16], ui
 template <int FA, int FB, int OPA = 0, int OPB = 0>
 __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, OPA, sa, OPB, sb);
+}
+
+// Two fp32 values -> two E4M3 bytes written into the low (HI=false) or high
+// (HI=true) 16 bits of `old`, after dividing by `scale` (|x/scale| <= 448).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_put2(uint32_t old, float a, float b, float scale) {
+  v2s o = __builtin_bit_cast(v2s, old);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, scale, HI);
+  return __builtin_bit_cast(uint32_t, o);
+}
+
+constexpr float kLazyRescale = 8.0f;   // log2 headroom before the accumulator is rescaled
+constexpr uint32_t kFp8Ones = 0x38383838u;   // four E4M3 1.0 bytes
+
+// Online-softmax step for one 16-query block and one 128-key tile, followed
+// by the two-term FP8 split of the probabilities ("MpFA免训练量化：QK4V8混合精度
+// 在Blackwell上的推理加速实践" §2.3: scores, normalizer and V accumulation in one
+// loop; §3.3: FP32 accumulator).
+//
+// S: the 8 QK^T subtile results of this lane (32 scores of query lane%16;
+//    masked entries -inf).  c = softmax_scale * log2(e).  m_run: running
+//    maximum in the log2 domain.  The running max only moves when it grows by
+//    more than kLazyRescale, so most tiles skip the rescale of O and L.
+// Outputs: Phi / Plo = the E4M3 codes of p / 2^X and of the residual
+//    (p - hi) / 2^(X-4), byte 4t+i holding subtile t, element i (the order of
+//    the FP8 MFMA k index), and psc = X + 127 (E8M0) with X chosen from the
+//    tile's largest p so that p / 2^X < 256.
+template <int ND>
+__device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run, v4f (&O)[ND], v4f& L, v8i& Phi,
+                                             v8i& Plo, int& psc) {
+  // row maximum over the lane's 32 scores (three-input maxima), then across
+  // the 4 lanes that hold the same query
+  float mx = S[0][0];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = (t == 0 ? 1 : 0); i < 4; ++i) mx = fmaxf(mx, S[t][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float tmax = mx * c;
+  const float m_new = fmaxf(m_run, tmax);
+  // wave-uniform, rarely taken: move the running max only when it grew by more
+  // than kLazyRescale somewhere in the wave
+  const bool grow = __builtin_amdgcn_readfirstlane((int)__any(m_new > m_run + kLazyRescale)) != 0;
+  if (__builtin_expect(grow, 0)) {
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) O[dd] *= alpha;
+    L *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+  const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
+  psc = X + 127;
+  const float sh = exp2i(X), sl = exp2i(X - 4);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(S[t][i], c, -m_use));
+    // the previous tile's codes are dead here: overwrite them in place
+    uint32_t h = e4m3_put2<false>((uint32_t)Phi[t], p[0], p[1], sh);
+    h = e4m3_put2<true>(h, p[2], p[3], sh);
+    const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, false);
+    const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, true);
+    uint32_t l = e4m3_put2<false>((uint32_t)Plo[t], p[0] - b01[0], p[1] - b01[1], sl);
+    l = e4m3_put2<true>(l, p[2] - b23[0], p[3] - b23[1], sl);
+    Phi[t] = (int)h;
+    Plo[t] = (int)l;
+  }
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -59,7 +59,7 @@ def test_decode_parity(gpu, B, Hq, Hkv, q_len, kv_len, cap, d, R, splits, ragged
     ro, rl = oatt.qk4v8_decode(q, rkc, rks, rvc.reshape(B, Hkv, cap, d), rvs.reshape(B, Hkv, -1), lens, R,
                                1 / math.sqrt(d))
     assert_attn_close(from_dev_bf16(o), ro, "decode")
-    assert np.abs(l.cpu().numpy() - rl).max() < 2e-3
+    assert np.abs(l.cpu().numpy() - rl).max() < 5e-3    # normalizer from the FP8 weights (rel. error <= 2^-8)
 
 
 def test_decode_split_count_and_prefill_agree(gpu):

@@ -49,7 +49,7 @@ def test_prefill_parity(gpu, B, Hq, Hkv, Nq, Nk, d, causal, R):
     q, k, v = _inputs(B, Hq, Hkv, Nq, Nk, d, seed=B * 1000 + Nq + Nk + d)
     o, l, ro, rl = _run(q, k, v, causal, R)
     assert_attn_close(o, ro, f"prefill {B},{Hq},{Hkv},{Nq},{Nk},{d},{causal},{R}")
-    assert np.abs(l - rl).max() < 2e-3
+    assert np.abs(l - rl).max() < 5e-3    # normalizer = sum of the two-term FP8 weights (rel. error <= 2^-8)
 
 
 def test_prefill_tiny_workload(gpu):
