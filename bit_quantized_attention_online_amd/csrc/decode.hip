@@ -195,11 +195,13 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
     }
     // ---- mask: keys past this row's limit (covers kv_len and the causal block) ----
     if (j0 + 127 > kvlen - a.q_len || !row_ok) {
+      // key(t, 4*lg + i) = 16*lg + subtile_key(t, i)
+      const int lim_l = lim - j0 - 16 * lg;
+      static_for<8>([&](auto T) {
+        constexpr int t = decltype(T)::value;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (j0 + subtile_key(t, 4 * lg + i) > lim) S[t][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) S[t][i] = mask_score(S[t][i], lim_l - subtile_key(t, i));
+      });
     }
     // ---- online softmax + two-term FP8 P ----
     int psc;

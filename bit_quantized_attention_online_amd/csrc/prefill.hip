@@ -9,22 +9,24 @@
 //
 // Structure on the GPU:
 //  1. pack_k: K -> MXFP4, written once per call into the workspace in the
-//     exact lane order of the QK^T MFMA A operand (16 B per lane per subtile).
+//     exact lane order of the QK^T MFMA A operand (16 B per lane).
 //  2. vtile_scale + pack_v: V -> per-tile E8M0 + E4M3 codes, written
 //     transposed (keys contiguous per head_dim column) in the lane order of
 //     the P·V MFMA A operand.
 //  3. attn: one workgroup of 8 waves per (batch, KV head, head group,
 //     position block); every wave owns 32 query rows of one query head, all
-//     waves of the workgroup share each 128-key K/V tile staged in LDS
-//     (double-buffered).  Per tile and wave:
-//       S^T = K·Q^T on v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 x FP4),
+//     waves share each 128-key K/V tile staged in LDS.  Per tile and wave:
+//       S^T = K·Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 x FP4),
 //       FP32 online softmax in the log2 domain with lazy rescaling,
 //       P split into two E4M3 terms (hi + residual) with a per-(row, tile)
 //       E8M0 range scale,
-//       O^T += V^T·P^T on the same instruction in FP8 x FP8 (twice: hi, lo).
+//       O^T += V^T·P^T on the same instruction in FP8 x FP8 (twice: hi, lo),
+//       and the row sums of the quantized weights as 1·P^T.
 //     Computing S^T and O^T (instead of S and O) puts one query per lane
 //     column in both, so the softmax state, the P operand and the output rows
-//     need no cross-lane transposes.
+//     need no cross-lane transposes.  The 32x32x64 shape keeps the matrix
+//     core busy long enough per instruction for the vector ALU work of the
+//     other wave on the SIMD to issue alongside it.
 #include "qk4v8_device.h"
 #include "qk4v8_launch.h"
 
@@ -32,18 +34,19 @@ namespace qk4v8 {
 
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
+constexpr int kWaves = 8;                 // waves per attention workgroup (two ping-pong groups)
 constexpr int kRowsPerWave = 32;          // two 16-row query blocks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Key offset (0..127 in a KV tile) held by row r of S^T subtile t.  Chosen so
-// that the 32 scores a lane holds after the 8 QK^T MFMAs are exactly the 32
-// keys the FP8 P·V MFMA expects in that lane (keys 16g..16g+15 and
-// 64+16g..64+16g+15 for lane group g), in byte order 4t + i.
-__host__ __device__ constexpr int subtile_key(int t, int r) {
-  return (t >> 2) * 64 + 16 * (r >> 2) + 4 * (t & 3) + (r & 3);
+// Key offset (0..127 in a KV tile) of row rho of the QK^T output for key block
+// kb (32 keys each).  The 32x32 result puts row (i/4)*8 + 4h + i%4 in element
+// i of lane (q, h); with this order that element is key 32*kb + 16*h + i, so
+// the 64 scores of lane (q, h) are exactly the keys 64*s2 + 32*(j/16) + 16*h
+// + j%16 (j = 0..31, s2 = kb/2) that the FP8 P·V MFMA expects from it, in
+// byte order j = 16*(kb%2) + i.
+__host__ __device__ constexpr int block_key(int kb, int rho) {
+  return 32 * kb + 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
 }
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -57,7 +60,7 @@ PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, i
   L.n_vtiles = (seq_k + v_tile_rows - 1) / v_tile_rows;
   size_t off = 0;
   L.off_k = off;     off = align_up(off + (size_t)bk * L.n_tiles * kKvTile * (head_dim / 2));
-  L.off_ks = off;    off = align_up(off + (size_t)bk * L.n_tiles * (head_dim / 32) * 16 * 8);
+  L.off_ks = off;    off = align_up(off + (size_t)bk * L.n_tiles * 256 * (head_dim / 64));
   L.off_v = off;     off = align_up(off + (size_t)bk * L.n_tiles * kKvTile * head_dim);
   L.off_vs = off;    off = align_up(off + (size_t)bk * L.n_tiles * 4);
   L.off_vtile = off; off = align_up(off + (size_t)bk * L.n_vtiles);
@@ -68,15 +71,17 @@ PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, i
 // ---------------------------------------------------------------------------
 // Pre-pass 1: K -> MXFP4 in MFMA-operand order.
 // Thread per (group bk, padded key j, 32-element block g).  Keys past seq_k
-// are written as zero codes.
-//   codes: [bk][tile][t][g][r][16 B]   scales: [bk][tile][g*16 + r][t]
+// are written as zero codes.  With NS = D/64 contraction steps, block g is
+// step s = g/2 of lane half h = g%2:
+//   codes : [bk][tile][kb][s][lane = rho + 32h][16 B]
+//   scales: [bk][tile][lane][kb*NS + s]
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict__ k, int64_t ks0, int64_t ks1,
                                                      int64_t ks2, int kv_heads, int seq_k, int64_t n_tiles,
                                                      uint8_t* __restrict__ wk, uint8_t* __restrict__ wks,
                                                      int64_t total) {
-  constexpr int NB = D / 32;
+  constexpr int NB = D / 32, NS = D / 64;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= total) return;
   const int g = (int)(id % NB);
@@ -85,25 +90,26 @@ __global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict_
   const int64_t b = bk / kv_heads, h = bk - b * kv_heads;
   const int64_t tile = jj / kKvTile;
   const int kk = (int)(jj - tile * kKvTile);
-  // invert subtile_key: kk = 64a + 16b + 4c + e  ->  t = 4a + c, r = 4b + e
-  const int t = 4 * (kk >> 6) + ((kk >> 2) & 3);
-  const int r = 4 * ((kk >> 4) & 3) + (kk & 3);
+  // invert block_key: kk = 32*kb + 16*hh + i  ->  rho = (i/4)*8 + 4*hh + i%4
+  const int kb = kk >> 5, hh = (kk >> 4) & 1, i = kk & 15;
+  const int rho = (i >> 2) * 8 + 4 * hh + (i & 3);
+  const int step = g >> 1, lane = rho + 32 * (g & 1);
   uint32_t codes[4] = {0, 0, 0, 0};
   uint32_t scale = 127;
   if (jj < seq_k) {
     const uint4* src = reinterpret_cast<const uint4*>(k + b * ks0 + h * ks1 + jj * ks2 + 32 * g);
     uint32_t w[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 x = src[i];
-      w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+    for (int q = 0; q < 4; ++q) {
+      const uint4 x = src[q];
+      w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
     }
     scale = mxfp4_quantize32(w, codes);
   }
   const int64_t tb = bk * n_tiles + tile;
-  *reinterpret_cast<uint4*>(wk + ((tb * 8 + t) * (NB * 16) + g * 16 + r) * 16) =
+  *reinterpret_cast<uint4*>(wk + ((tb * 4 + kb) * NS + step) * 1024 + lane * 16) =
       make_uint4(codes[0], codes[1], codes[2], codes[3]);
-  wks[(tb * (NB * 16) + g * 16 + r) * 8 + t] = (uint8_t)scale;
+  wks[(tb * 64 + lane) * (4 * NS) + kb * NS + step] = (uint8_t)scale;
 }
 
 // ---------------------------------------------------------------------------
@@ -141,8 +147,8 @@ __global__ void __launch_bounds__(256) vtile_scale_kernel(const uint16_t* __rest
 // Pre-pass 3: V -> E4M3 codes, transposed per 128-key tile.
 // One workgroup per (group, tile): quantize row-major into LDS, then gather
 // 16 consecutive keys of one column per output chunk.
-//   codes : [bk][tile][dd = D/16][half][g][m][16 keys]  (column d = 16dd+m,
-//           keys 64*half + 16g .. +15)
+//   codes : [bk][tile][db = D/32][s2][half][lane = m + 32h][16 keys]
+//           (column d = 32*db + m, keys 64*s2 + 32*half + 16*h .. +15)
 //   scales: [bk][tile] u32, byte b = E8M0 of the V tile holding key 32b
 // ---------------------------------------------------------------------------
 template <int D>
@@ -176,12 +182,10 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict_
     dst[1] = hi;
   }
   __syncthreads();
-  constexpr int ND = D / 16;
   uint8_t* out = wv + (bk * n_tiles + tile) * (int64_t)(kKvTile * D);
-  for (int o = threadIdx.x; o < ND * 128; o += 256) {
-    const int dd = o >> 7, half = (o >> 6) & 1, lane = o & 63;
-    const int g = lane >> 4, m = lane & 15;
-    const int col = dd * 16 + m, k0 = half * 64 + g * 16;
+  for (int o = threadIdx.x; o < D * 8; o += 256) {
+    const int lane = o & 63, half = (o >> 6) & 1, s2 = (o >> 7) & 1, db = o >> 8;
+    const int col = db * 32 + (lane & 31), k0 = 64 * s2 + 32 * half + 16 * (lane >> 5);
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -224,24 +228,41 @@ struct AttnArgs {
 
 template <int D>
 struct TileBytes {
-  static constexpr int NB = D / 32;
-  static constexpr int K = 8 * NB * 16 * 16;      // codes of one 128-key tile
-  static constexpr int KS = NB * 16 * 8;          // K scales of one tile
+  static constexpr int NS = D / 64;               // 64-wide contraction steps of QK^T
+  static constexpr int K = 4 * NS * 1024;         // codes of one 128-key tile
+  static constexpr int KS = 64 * 4 * NS;          // K scales of one tile
   static constexpr int V = kKvTile * D;           // V^T codes of one tile
   static constexpr int STAGE = K + KS + V + 16;   // + V scale word (padded)
 };
 
+// Ping-pong schedule.  The 8 waves form two groups of 4 (one wave of each on
+// every SIMD).  Per KV tile k a group runs an MFMA step (P·V of tile k-1, then
+// QK^T of tile k) and a VALU step (mask + softmax + FP8 split of tile k),
+// separated by workgroup barriers.  Both groups run the same instruction
+// stream, but group 1 starts one barrier late (group 0 takes one extra barrier
+// at the end), so in every phase one wave per SIMD feeds the matrix core while
+// the other keeps the vector ALU busy.  Tile k is read in phases 2k .. 2k+3,
+// so three LDS stages rotate.  Each thread fetches its share of tile k+1 into
+// registers at the start of its iteration k; group 0 writes it to LDS after
+// its VALU step and group 1 after its MFMA step, both at the end of phase
+// 2k+1, before either group's QK^T of tile k+1.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_kernel(AttnArgs a) {
+  constexpr int W = 8;
+  constexpr int kThreads = W * 64;
   using TB = TileBytes<D>;
-  constexpr int NB = TB::NB;
-  constexpr int ND = D / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TB::STAGE];
+  constexpr int NS = TB::NS;        // QK^T contraction steps (64 head_dim each)
+  constexpr int NDB = D / 32;       // 32-row head_dim blocks of O^T
+  constexpr int kStages = 3;
+  constexpr int kOnes = kStages * TB::STAGE;   // 1 KB of E4M3 1.0: the row-sum MFMA operand
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * TB::STAGE + 1024];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int ql = lane & 15;     // query column of this lane within a 16-block
-  const int lg = lane >> 4;     // lane group (k-block / d sub-row group)
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;    // 0: MFMA step first, 1: one phase behind
+  const int ql = lane & 31;     // query column of this lane
+  const int lh = lane >> 5;     // lane half (k-block of the MFMA operands)
 
   // workgroup -> (b, kv head, head group); position block reversed so the
   // longest causal rows start first
@@ -257,16 +278,15 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
   const int p0w = P0 + pb * kRowsPerWave;
   const int off = a.seq_k - a.seq_q;
 
-  // key range of the workgroup and of this wave
+  // every wave walks the workgroup's tiles; rows that cannot see a tile's
+  // keys are masked
   const int wg_last_row = min(P0 + a.pos_blocks * kRowsPerWave, a.seq_q) - 1;
   const int kend_wg = CAUSAL ? min(a.seq_k, wg_last_row + off + 1) : a.seq_k;
-  const int nt_wg = (kend_wg + kKvTile - 1) / kKvTile;
+  const int nt = (kend_wg + kKvTile - 1) / kKvTile;
   const bool wave_live = p0w < a.seq_q;
-  const int w_last_row = min(p0w + kRowsPerWave, a.seq_q) - 1;
-  const int kend_w = wave_live ? (CAUSAL ? min(a.seq_k, w_last_row + off + 1) : a.seq_k) : 0;
-  const int nt_w = (kend_w + kKvTile - 1) / kKvTile;
-  // tiles whose last key exceeds this bound need the element mask
-  const int mask_lim = CAUSAL ? min(a.seq_k - 1, p0w + off) : a.seq_k - 1;
+  const int mask_lim = CAUSAL ? min(a.seq_k - 1, p0w + off) : a.seq_k - 1;   // tiles past it need the mask
+  const int row = p0w + ql;
+  const int row_lim = (CAUSAL ? min(a.seq_k - 1, row + off) : a.seq_k - 1) - 16 * lh;
 
   const int64_t bk = (int64_t)b * a.kv_heads + kvh;
   const uint8_t* gk = a.wk + bk * a.n_tiles * TB::K;
@@ -274,18 +294,17 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
   const uint8_t* gv = a.wv + bk * a.n_tiles * TB::V;
   const uint32_t* gvs = a.wvs + bk * a.n_tiles;
 
-  // ---- Q prologue: quantize this wave's 32 rows to MXFP4 in registers.
-  // Lanes of k-blocks past head_dim (D = 64) hold zero codes, so whatever K
-  // codes those lanes read contribute nothing.
-  v8i qf[2];
-  int qsc[2];
+  // ---- Q prologue: this wave's 32 rows to MXFP4 in registers; lane (q, h)
+  // holds head_dim block 2s + h of row q for contraction step s ----
+  v8i qf[NS];
+  int qsc[NS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int st = 0; st < NS; ++st) {
     uint4 qc = make_uint4(0, 0, 0, 0);
-    qsc[qb] = 127;
-    const int row = p0w + qb * 16 + ql;
-    if (row < a.seq_q && lg < NB) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.q + b * a.qs0 + (int64_t)head * a.qs1 + row * a.qs2 + 32 * lg);
+    qsc[st] = 127;
+    if (row < a.seq_q) {
+      const uint4* src =
+          reinterpret_cast<const uint4*>(a.q + b * a.qs0 + (int64_t)head * a.qs1 + row * a.qs2 + 32 * (2 * st + lh));
       uint32_t w[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -293,145 +312,154 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
         w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
       }
       uint32_t c[4];
-      qsc[qb] = (int)mxfp4_quantize32(w, c);
+      qsc[st] = (int)mxfp4_quantize32(w, c);
       qc = make_uint4(c[0], c[1], c[2], c[3]);
     }
-    qf[qb] = fp4_operand(qc);
+    qf[st] = fp4_operand(qc);
   }
 
-  v4f O[2][ND];
-  v4f L[2];
+  v16f O[NDB];
+  v16f L = v16f{};
+  v16f S[4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    L[qb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dd = 0; dd < ND; ++dd) O[qb][dd] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-  float m_run[2] = {-INFINITY, -INFINITY};
+  for (int db = 0; db < NDB; ++db) O[db] = v16f{};
+  float m_run = -INFINITY;
   v8i Phi[2] = {v8i{}, v8i{}}, Plo[2] = {v8i{}, v8i{}};
-  const v8i ones = v8i{(int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones,
-                       (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones};
-  const int klane = lane & (NB * 16 - 1);   // K fragment lane (D = 64 reuses lanes 0..31)
+  int psc = 127;
+  if (tid < 256) reinterpret_cast<uint32_t*>(lds + kOnes)[tid] = kFp8Ones;
 
-  // ---- tile staging: global -> registers -> LDS (double-buffered LDS) ----
+  // output addressing, computed here so the argument block is dead in the loop
+  uint16_t* const orow = a.o + b * a.os0 + (int64_t)head * a.os1 + (int64_t)row * a.os2;
+  float* const lse_row = a.lse ? a.lse + ((int64_t)b * a.q_heads + head) * a.seq_q + row : nullptr;
+  const bool row_live = row < a.seq_q;
+  const float cexp = a.c;
+
+  // ---- tile staging: global -> registers -> LDS.  The staging arrays are
+  // clang vectors indexed only at compile time, so they stay in VGPRs. ----
   constexpr int KV4 = TB::K / 16, VV4 = TB::V / 16, KSV4 = TB::KS / 16;
-  uint4 rk = make_uint4(0, 0, 0, 0), rv0 = rk, rv1 = rk, rks = rk;
+  constexpr int KPT = (KV4 + kThreads - 1) / kThreads, VPT = (VV4 + kThreads - 1) / kThreads;
+  v4i rk[KPT], rv[VPT], rks;
   uint32_t rvs = 0;
-#define QK4V8_GLOAD(tile)                                                                    \
-  do {                                                                                       \
-    const uint4* sk_ = reinterpret_cast<const uint4*>(gk + (int64_t)(tile) * TB::K);        \
-    const uint4* sv_ = reinterpret_cast<const uint4*>(gv + (int64_t)(tile) * TB::V);        \
-    const uint4* sks_ = reinterpret_cast<const uint4*>(gks + (int64_t)(tile) * TB::KS);     \
-    if (tid < KV4) rk = sk_[tid];                                                            \
-    if (tid < VV4) rv0 = sv_[tid];                                                           \
-    if (tid + kThreads < VV4) rv1 = sv_[tid + kThreads];                                     \
-    if (tid < KSV4) rks = sks_[tid];                                                         \
-    if (tid == 0) rvs = gvs[(tile)];                                                         \
-  } while (0)
-#define QK4V8_SSTORE(buf)                                                                    \
-  do {                                                                                       \
-    uint8_t* base_ = lds + (buf) * TB::STAGE;                                                \
-    if (tid < KV4) reinterpret_cast<uint4*>(base_)[tid] = rk;                                \
-    if (tid < VV4) reinterpret_cast<uint4*>(base_ + TB::K + TB::KS)[tid] = rv0;              \
-    if (tid + kThreads < VV4) reinterpret_cast<uint4*>(base_ + TB::K + TB::KS)[tid + kThreads] = rv1; \
-    if (tid < KSV4) reinterpret_cast<uint4*>(base_ + TB::K)[tid] = rks;                      \
-    if (tid == 0) *reinterpret_cast<uint32_t*>(base_ + TB::K + TB::KS + TB::V) = rvs;        \
-  } while (0)
+  auto gload = [&](int tile) __attribute__((always_inline)) {
+    const v4i* sk = reinterpret_cast<const v4i*>(gk + (int64_t)tile * TB::K);
+    const v4i* sv = reinterpret_cast<const v4i*>(gv + (int64_t)tile * TB::V);
+    static_for<KPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if (KV4 % kThreads == 0 || tid + i * kThreads < KV4) rk[i] = sk[tid + i * kThreads];
+    });
+    static_for<VPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if (VV4 % kThreads == 0 || tid + i * kThreads < VV4) rv[i] = sv[tid + i * kThreads];
+    });
+    if (tid < KSV4) rks = reinterpret_cast<const v4i*>(gks + (int64_t)tile * TB::KS)[tid];
+    if (tid == 0) rvs = gvs[tile];
+  };
+  auto sstore = [&](int stage) __attribute__((always_inline)) {
+    uint8_t* base = lds + stage * TB::STAGE;
+    static_for<KPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if (KV4 % kThreads == 0 || tid + i * kThreads < KV4) reinterpret_cast<v4i*>(base)[tid + i * kThreads] = rk[i];
+    });
+    static_for<VPT>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if (VV4 % kThreads == 0 || tid + i * kThreads < VV4)
+        reinterpret_cast<v4i*>(base + TB::K + TB::KS)[tid + i * kThreads] = rv[i];
+    });
+    if (tid < KSV4) reinterpret_cast<v4i*>(base + TB::K)[tid] = rks;
+    if (tid == 0) *reinterpret_cast<uint32_t*>(base + TB::K + TB::KS + TB::V) = rvs;
+  };
 
-  if (nt_wg > 0) {
-    QK4V8_GLOAD(0);
-    QK4V8_SSTORE(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < nt_wg; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nt_wg) QK4V8_GLOAD(j + 1);
-    if (j < nt_w) {
-      const uint8_t* base = lds + buf * TB::STAGE;
-      const uint8_t* lk = base;
-      const uint8_t* lks = base + TB::K;
+  // MFMA step k: O^T += V^T·P^T and L += 1·P^T for tile k-1 (FP8 x FP8),
+  // then S^T = K·Q^T for tile k (FP4 x FP4; both operands' E8M0 scales are
+  // applied inside the instruction, so the scores come out dequantized).
+  auto mfma_step = [&](int k) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    if (k >= 1) {
+      const uint8_t* base = lds + ((k - 1) % kStages) * TB::STAGE;
       const uint8_t* lv = base + TB::K + TB::KS;
       const uint32_t vsw = *reinterpret_cast<const uint32_t*>(base + TB::K + TB::KS + TB::V);
-
-      // ---- S^T = K · Q^T  (FP4 x FP4; both operands' E8M0 scales applied
-      // inside the instruction, i.e. the scores come out dequantized) ----
-      v4f S[2][8];
-      const uint2 ksc = *reinterpret_cast<const uint2*>(lks + klane * 8);
-      static_for<8>([&](auto T) {
-        constexpr int t = decltype(T)::value;
-        const v8i af = fp4_operand(*reinterpret_cast<const uint4*>(lk + (t * NB * 16 + klane) * 16));
-        const int sa = (int)(t < 4 ? ksc.x : ksc.y);
+      const v4i o0 = *reinterpret_cast<const v4i*>(lds + kOnes + (lane & 31) * 16);
+      const v8i ones = __builtin_shufflevector(o0, o0, 0, 1, 2, 3, 0, 1, 2, 3);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          S[qb][t] = mfma16x16x128<kFmtFp4, kFmtFp4, t & 3, 0>(af, qf[qb], v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc[qb]);
-      });
-
-      // ---- mask (only tiles that cross the causal diagonal or seq_k) ----
-      if (j * kKvTile + kKvTile - 1 > mask_lim) {
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int vsc = (int)((vsw >> (8 * (2 * s2 + lh))) & 0xFF);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int row = p0w + qb * 16 + ql;
-          const int lim = (CAUSAL ? min(a.seq_k - 1, row + off) : a.seq_k - 1) - j * kKvTile;
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (subtile_key(t, 4 * lg + i) > lim) S[qb][t][i] = -INFINITY;
+        for (int db = 0; db < NDB; ++db) {
+          const uint8_t* src = lv + (db * 2 + s2) * 2048 + lane * 16;
+          const v4i v0 = *reinterpret_cast<const v4i*>(src);
+          const v4i v1 = *reinterpret_cast<const v4i*>(src + 1024);
+          const v8i av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          O[db] = mfma32x32x64<kFmtFp8, kFmtFp8>(av, Phi[s2], O[db], vsc, psc);
+          O[db] = mfma32x32x64<kFmtFp8, kFmtFp8>(av, Plo[s2], O[db], vsc, psc - 4);
         }
-      }
-
-      // ---- online softmax and two-term FP8 P ----
-      int psc[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) softmax_tile<ND>(S[qb], a.c, m_run[qb], O[qb], L[qb], Phi[qb], Plo[qb], psc[qb]);
-
-      // ---- O^T += V^T · P^T and L += 1 · P^T  (FP8 x FP8) ----
-      const int vsc = (int)((vsw >> (8 * lg)) & 0xFF);
-#pragma unroll
-      for (int dd = 0; dd < ND; ++dd) {
-        const uint4 v0 = *reinterpret_cast<const uint4*>(lv + ((dd * 2 + 0) * 64 + lane) * 16);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(lv + ((dd * 2 + 1) * 64 + lane) * 16);
-        const v8i av = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          O[qb][dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(av, Phi[qb], O[qb][dd], vsc, psc[qb]);
-          O[qb][dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(av, Plo[qb], O[qb][dd], vsc, psc[qb] - 4);
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        L[qb] = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Phi[qb], L[qb], 127, psc[qb]);
-        L[qb] = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Plo[qb], L[qb], 127, psc[qb] - 4);
+        L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[s2], L, 127, psc);
+        L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[s2], L, 127, psc - 4);
       }
     }
-    if (j + 1 < nt_wg) QK4V8_SSTORE(buf ^ 1);
+    if (k < nt) {
+      const uint8_t* base = lds + (k % kStages) * TB::STAGE;
+      const uint32_t* ksw = reinterpret_cast<const uint32_t*>(base + TB::K + lane * (4 * NS));
+      uint32_t ks[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) ks[i] = ksw[i];
+      static_for<4 * NS>([&](auto I) {
+        constexpr int idx = decltype(I)::value;           // kb * NS + st
+        constexpr int kb = idx / NS, st = idx % NS;
+        const v8i af = fp4_operand(*reinterpret_cast<const uint4*>(base + (idx * 64 + lane) * 16));
+        S[kb] = mfma32x32x64<kFmtFp4, kFmtFp4, idx & 3, 0>(af, qf[st], st == 0 ? v16f{} : S[kb],
+                                                          (int)ks[idx >> 2], qsc[st]);
+      });
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // VALU step k: mask, online softmax and two-term FP8 split of tile k.
+  auto valu_step = [&](int k) __attribute__((always_inline)) {
+    if (k < 0 || k >= nt) return;
+    if (k * kKvTile + kKvTile - 1 > mask_lim) {      // tiles crossing the diagonal or seq_k
+      // element i of key block kb in this lane is key 32*kb + 16*h + i
+      const int lim = row_lim - k * kKvTile;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kb][i] = mask_score(S[kb][i], lim - (32 * kb + i));
+    }
+    softmax_tile32<NDB>(S, cexp, m_run, O, L, Phi, Plo, psc);
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  if (grp == 1) __syncthreads();       // group 1 runs one phase behind
+  for (int k = 0; k <= nt; ++k) {
+    const bool next = k + 1 < nt;
+    if (next) gload(k + 1);
+    mfma_step(k);
+    if (grp == 1 && next) sstore((k + 1) % kStages);
+    __syncthreads();
+    valu_step(k);
+    if (grp == 0 && next) sstore((k + 1) % kStages);
     __syncthreads();
   }
-#undef QK4V8_GLOAD
-#undef QK4V8_SSTORE
+  if (grp == 0) __syncthreads();       // matches group 1's initial wait
 
   // ---- epilogue: normalize by the sum of the quantized weights, store bf16
-  // rows and the log-sum-exp ----
-  if (!wave_live) return;
+  // rows and the log-sum-exp.  Element i of head_dim block db in lane (q, h)
+  // is column 32*db + 8*(i/4) + 4*h + i%4. ----
+  if (!wave_live || !row_live) return;
+  const float l = L[0];     // every row of the ones-MFMA holds the same sum
+  const float inv = 1.0f / l;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float l = L[qb][0];     // every row of the ones-MFMA holds the same sum
-    const int row = p0w + qb * 16 + ql;
-    if (row >= a.seq_q) continue;
-    const float inv = 1.0f / l;
-    uint16_t* dst = a.o + b * a.os0 + (int64_t)head * a.os1 + row * a.os2;
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int dd = 0; dd < ND; ++dd) {
-      const v4f x = O[qb][dd] * inv;
-      const uint32_t w0 = f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16);
-      const uint32_t w1 = f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16);
-      *reinterpret_cast<uint2*>(dst + dd * 16 + 4 * lg) = make_uint2(w0, w1);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const uint32_t w0 = f32_to_bf16(O[db][4 * g4] * inv) | (f32_to_bf16(O[db][4 * g4 + 1] * inv) << 16);
+      const uint32_t w1 = f32_to_bf16(O[db][4 * g4 + 2] * inv) | (f32_to_bf16(O[db][4 * g4 + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + 32 * db + 8 * g4 + 4 * lh) = make_uint2(w0, w1);
     }
-    if (a.lse != nullptr && lg == 0) {
-      const float m_use = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-      a.lse[((int64_t)b * a.q_heads + head) * a.seq_q + row] = (m_use + __log2f(l)) * kLn2;
-    }
+  if (lse_row != nullptr && lh == 0) {
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    *lse_row = (m_use + __log2f(l)) * kLn2;
   }
 }
 
@@ -478,9 +506,9 @@ static hipError_t launch_attn_d(const PrefillParams& p, hipStream_t stream) {
   a.pos_groups = (p.seq_q + rows_per_wg - 1) / rows_per_wg;
   const dim3 grid((unsigned)((int64_t)a.xblocks * a.pos_groups));
   if (p.causal)
-    hipLaunchKernelGGL((attn_kernel<D, true>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<D, true>), grid, dim3(kWaves * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, false>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<D, false>), grid, dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

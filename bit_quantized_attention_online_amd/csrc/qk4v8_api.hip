@@ -8,7 +8,7 @@
 #include <cmath>
 #include <cstring>
 
-#include "../../include/qk4v8.h"
+#include "qk4v8.h"
 #include "qk4v8_launch.h"
 
 using namespace qk4v8;

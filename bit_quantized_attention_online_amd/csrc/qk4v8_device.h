@@ -30,6 +30,7 @@ namespace qk4v8 {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v2s __attribute__((ext_vector_type(2)));
 
 // Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(<N-1>), so the
@@ -113,6 +114,11 @@ __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b, const v
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, OPA, sa, OPB, sb);
 }
 
+template <int FA, int FB, int OPA = 0, int OPB = 0>
+__device__ __forceinline__ v16f mfma32x32x64(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, OPA, sa, OPB, sb);
+}
+
 // Two fp32 values -> two E4M3 bytes written into the low (HI=false) or high
 // (HI=true) 16 bits of `old`, after dividing by `scale` (|x/scale| <= 448).
 template <bool HI>
@@ -120,6 +126,13 @@ __device__ __forceinline__ uint32_t e4m3_put2(uint32_t old, float a, float b, fl
   v2s o = __builtin_bit_cast(v2s, old);
   o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, scale, HI);
   return __builtin_bit_cast(uint32_t, o);
+}
+
+// Causal / length mask without compare masks: slack >= 0 keeps the score,
+// slack < 0 turns it into -inf (min with +inf or -inf built from the sign bit).
+__device__ __forceinline__ float mask_score(float s, int slack) {
+  const float bound = __uint_as_float(((uint32_t)slack & 0x80000000u) | 0x7F800000u);
+  return fminf(s, bound);
 }
 
 constexpr float kLazyRescale = 8.0f;   // log2 headroom before the accumulator is rescaled
@@ -180,6 +193,52 @@ __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run,
     l = e4m3_put2<true>(l, p[2] - b23[0], p[3] - b23[1], sl);
     Phi[t] = (int)h;
     Plo[t] = (int)l;
+  }
+}
+
+// The same step for the 32x32x64 layout: S holds the 4 key-block results of
+// this lane (64 scores of query lane%32, split with lane^32), P byte j of the
+// 8-dword operand of P·V step s2 holds key-block 2*s2 + j/16, element j%16.
+template <int NO>
+__device__ __forceinline__ void softmax_tile32(v16f (&S)[4], float c, float& m_run, v16f (&O)[NO], v16f& L,
+                                               v8i (&Phi)[2], v8i (&Plo)[2], int& psc) {
+  float mx = S[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = (kb == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, S[kb][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float tmax = mx * c;
+  const float m_new = fmaxf(m_run, tmax);
+  const bool grow = __builtin_amdgcn_readfirstlane((int)__any(m_new > m_run + kLazyRescale)) != 0;
+  if (__builtin_expect(grow, 0)) {
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int o = 0; o < NO; ++o) O[o] *= alpha;
+    L *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+  const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
+  psc = X + 127;
+  const float sh = exp2i(X), sl = exp2i(X - 4);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(S[kb][4 * w + e], c, -m_use));
+      const int dw = 4 * (kb & 1) + w;
+      uint32_t h = e4m3_put2<false>((uint32_t)Phi[kb >> 1][dw], p[0], p[1], sh);
+      h = e4m3_put2<true>(h, p[2], p[3], sh);
+      const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, false);
+      const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, true);
+      uint32_t l = e4m3_put2<false>((uint32_t)Plo[kb >> 1][dw], p[0] - b01[0], p[1] - b01[1], sl);
+      l = e4m3_put2<true>(l, p[2] - b23[0], p[3] - b23[1], sl);
+      Phi[kb >> 1][dw] = (int)h;
+      Plo[kb >> 1][dw] = (int)l;
+    }
   }
 }
 
