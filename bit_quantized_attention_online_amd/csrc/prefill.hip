@@ -13,6 +13,9 @@
 //  2. vtile_scale + pack_v: V -> per-tile E8M0 + E4M3 codes, written
 //     transposed (keys contiguous per head_dim column) in the lane order of
 //     the P·V MFMA A operand.
+//     Both write one contiguous record per (batch x KV head, 128-key tile):
+//     K codes | 1 KB of scales | V codes, i.e. the tile's LDS image, so the
+//     attention kernel moves it with direct global->LDS loads in 1 KB chunks.
 //  3. attn: one workgroup of 8 waves per (batch, KV head, head group,
 //     position block); every wave owns 32 query rows of one query head, all
 //     waves share each 128-key K/V tile staged in LDS.  Per tile and wave:
@@ -51,18 +54,69 @@ __host__ __device__ constexpr int block_key(int kb, int rho) {
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// vmcnt(N) on gfx9: vm_cnt[3:0] | exp_cnt[6:4] | lgkm_cnt[11:8] | vm_cnt[5:4]
+// << 14, the other counters left at their maximum (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base is wave-uniform).  Completion is tracked by
+// vmcnt, not by the compiler.
+__device__ __forceinline__ void global_to_lds16(const uint8_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                   reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                       reinterpret_cast<uintptr_t>(lds_base)),
+                                   16, 0, 0);
+}
+
+// Workgroup barrier inside the attention loop.  The LDS data it orders comes
+// from direct loads that each wave has already waited for, and every LDS read
+// before it has been consumed, so no memory fence is needed (a fence would
+// wait for the prefetches still in flight); the empty asm statements keep the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// An empty asm that reads x: the value has to be computed at this point of
+// the program, which pins pure computations (matrix instructions) in place.
+template <class T>
+__device__ __forceinline__ void keep_in_vgprs(const T& x) {
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("" ::"v"(x));
+#else
+  (void)x;
+#endif
+}
+
 }  // namespace
+
+// Bytes of one packed 128-key tile record (the LDS image of the tile).
+template <int D>
+struct TileBytes {
+  static constexpr int NS = D / 64;               // 64-wide contraction steps of QK^T
+  static constexpr int K = 4 * NS * 1024;         // K codes: [kb][step][lane][16 B]
+  static constexpr int SC = 1024;                 // K scales [lane][kb*NS+step], then the V scale word
+  static constexpr int KS = 64 * 4 * NS;          // K scale bytes at the start of SC
+  static constexpr int VS_OFF = 512;              // V scale word inside SC
+  static constexpr int V = kKvTile * D;           // V^T codes
+  static constexpr int REC = K + SC + V;          // a multiple of 1 KB
+  static constexpr int CHUNKS = REC / 1024;       // 1 KB direct-load chunks
+};
 
 PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, int v_tile_rows) {
   PrefillLayout L;
   const int64_t bk = (int64_t)batch * kv_heads;
   L.n_tiles = (seq_k + kKvTile - 1) / kKvTile;
   L.n_vtiles = (seq_k + v_tile_rows - 1) / v_tile_rows;
+  L.rec_bytes = head_dim == 64 ? TileBytes<64>::REC : TileBytes<128>::REC;
   size_t off = 0;
-  L.off_k = off;     off = align_up(off + (size_t)bk * L.n_tiles * kKvTile * (head_dim / 2));
-  L.off_ks = off;    off = align_up(off + (size_t)bk * L.n_tiles * 256 * (head_dim / 64));
-  L.off_v = off;     off = align_up(off + (size_t)bk * L.n_tiles * kKvTile * head_dim);
-  L.off_vs = off;    off = align_up(off + (size_t)bk * L.n_tiles * 4);
+  L.off_rec = off;   off = align_up(off + (size_t)bk * L.n_tiles * L.rec_bytes);
   L.off_vtile = off; off = align_up(off + (size_t)bk * L.n_vtiles);
   L.total = off;
   return L;
@@ -72,15 +126,15 @@ PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, i
 // Pre-pass 1: K -> MXFP4 in MFMA-operand order.
 // Thread per (group bk, padded key j, 32-element block g).  Keys past seq_k
 // are written as zero codes.  With NS = D/64 contraction steps, block g is
-// step s = g/2 of lane half h = g%2:
-//   codes : [bk][tile][kb][s][lane = rho + 32h][16 B]
-//   scales: [bk][tile][lane][kb*NS + s]
+// step s = g/2 of lane half h = g%2.  In the record of tile (bk, tile):
+//   codes : [kb][s][lane = rho + 32h][16 B]          at 0
+//   scales: [lane][kb*NS + s]                         at K
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict__ k, int64_t ks0, int64_t ks1,
                                                      int64_t ks2, int kv_heads, int seq_k, int64_t n_tiles,
-                                                     uint8_t* __restrict__ wk, uint8_t* __restrict__ wks,
-                                                     int64_t total) {
+                                                     uint8_t* __restrict__ rec, int64_t total) {
+  using TB = TileBytes<D>;
   constexpr int NB = D / 32, NS = D / 64;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= total) return;
@@ -106,10 +160,9 @@ __global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict_
     }
     scale = mxfp4_quantize32(w, codes);
   }
-  const int64_t tb = bk * n_tiles + tile;
-  *reinterpret_cast<uint4*>(wk + ((tb * 4 + kb) * NS + step) * 1024 + lane * 16) =
-      make_uint4(codes[0], codes[1], codes[2], codes[3]);
-  wks[(tb * 64 + lane) * (4 * NS) + kb * NS + step] = (uint8_t)scale;
+  uint8_t* r = rec + (bk * n_tiles + tile) * TB::REC;
+  *reinterpret_cast<uint4*>(r + (kb * NS + step) * 1024 + lane * 16) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+  r[TB::K + lane * (4 * NS) + kb * NS + step] = (uint8_t)scale;
 }
 
 // ---------------------------------------------------------------------------
@@ -146,16 +199,17 @@ __global__ void __launch_bounds__(256) vtile_scale_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------
 // Pre-pass 3: V -> E4M3 codes, transposed per 128-key tile.
 // One workgroup per (group, tile): quantize row-major into LDS, then gather
-// 16 consecutive keys of one column per output chunk.
-//   codes : [bk][tile][db = D/32][s2][half][lane = m + 32h][16 keys]
+// 16 consecutive keys of one column per output chunk.  In the tile record:
+//   codes : [db = D/32][s2][half][lane = m + 32h][16 keys]      at K + SC
 //           (column d = 32*db + m, keys 64*s2 + 32*half + 16*h .. +15)
-//   scales: [bk][tile] u32, byte b = E8M0 of the V tile holding key 32b
+//   scales: u32, byte b = E8M0 of the V tile holding key 32b    at K + VS_OFF
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict__ v, int64_t vs0, int64_t vs1,
                                                      int64_t vs2, int kv_heads, int seq_k, int R, int64_t n_tiles,
                                                      int64_t n_vtiles, const uint8_t* __restrict__ vtile,
-                                                     uint8_t* __restrict__ wv, uint32_t* __restrict__ wvs) {
+                                                     uint8_t* __restrict__ rec) {
+  using TB = TileBytes<D>;
   constexpr int LDSROW = D + 4;   // bytes per key row in LDS (padding spreads banks)
   __shared__ uint8_t tileb[kKvTile * LDSROW];
   const int64_t bk = blockIdx.x / n_tiles, tile = blockIdx.x - bk * n_tiles;
@@ -182,7 +236,8 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict_
     dst[1] = hi;
   }
   __syncthreads();
-  uint8_t* out = wv + (bk * n_tiles + tile) * (int64_t)(kKvTile * D);
+  uint8_t* const r = rec + (bk * n_tiles + tile) * TB::REC;
+  uint8_t* out = r + TB::K + TB::SC;
   for (int o = threadIdx.x; o < D * 8; o += 256) {
     const int lane = o & 63, half = (o >> 6) & 1, s2 = (o >> 7) & 1, db = o >> 8;
     const int col = db * 32 + (lane & 31), k0 = 64 * s2 + 32 * half + 16 * (lane >> 5);
@@ -204,7 +259,7 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict_
       if (j >= seq_k) j = seq_k - 1;
       s |= (uint32_t)vts[j / R] << (8 * blk);
     }
-    wvs[bk * n_tiles + tile] = s;
+    *reinterpret_cast<uint32_t*>(r + TB::K + TB::VS_OFF) = s;
   }
 }
 
@@ -215,24 +270,12 @@ struct AttnArgs {
   const uint16_t* q;
   uint16_t* o;
   float* lse;
-  const uint8_t* wk;
-  const uint8_t* wks;
-  const uint8_t* wv;
-  const uint32_t* wvs;
+  const uint8_t* rec;      // packed tile records [bk][tile]
   int64_t qs0, qs1, qs2, os0, os1, os2;
   int q_heads, kv_heads, group, heads_per_wg, pos_blocks, seq_q, seq_k;
   int xblocks, pos_groups;   // 1-D grid = pos_groups x xblocks, xblocks fastest
   int64_t n_tiles;
   float c;          // softmax_scale * log2(e)
-};
-
-template <int D>
-struct TileBytes {
-  static constexpr int NS = D / 64;               // 64-wide contraction steps of QK^T
-  static constexpr int K = 4 * NS * 1024;         // codes of one 128-key tile
-  static constexpr int KS = 64 * 4 * NS;          // K scales of one tile
-  static constexpr int V = kKvTile * D;           // V^T codes of one tile
-  static constexpr int STAGE = K + KS + V + 16;   // + V scale word (padded)
 };
 
 // Ping-pong schedule.  The 8 waves form two groups of 4 (one wave of each on
@@ -241,21 +284,24 @@ struct TileBytes {
 // separated by workgroup barriers.  Both groups run the same instruction
 // stream, but group 1 starts one barrier late (group 0 takes one extra barrier
 // at the end), so in every phase one wave per SIMD feeds the matrix core while
-// the other keeps the vector ALU busy.  Tile k is read in phases 2k .. 2k+3,
-// so three LDS stages rotate.  Each thread fetches its share of tile k+1 into
-// registers at the start of its iteration k; group 0 writes it to LDS after
-// its VALU step and group 1 after its MFMA step, both at the end of phase
-// 2k+1, before either group's QK^T of tile k+1.
+// the other keeps the vector ALU busy.  Tile k is read in phases 2k .. 2k+3.
+//
+// Tiles reach LDS by direct global->LDS loads (no registers involved): every
+// wave copies its share of the 1 KB chunks of tile k+2 at the start of its
+// iteration k, into stage (k+2) % 4, whose previous tile k-2 was last read in
+// phase 2k-1.  Before the barrier that ends phase 2k+1 every wave waits until
+// its chunks of tile k+1 have landed (the loads complete in order, so at most
+// its chunks of tile k+2 may still be in flight), which publishes tile k+1
+// before its first QK^T in phase 2k+2.  A tile thus has about three phases to
+// arrive.
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_kernel(AttnArgs a) {
-  constexpr int W = 8;
-  constexpr int kThreads = W * 64;
   using TB = TileBytes<D>;
   constexpr int NS = TB::NS;        // QK^T contraction steps (64 head_dim each)
   constexpr int NDB = D / 32;       // 32-row head_dim blocks of O^T
-  constexpr int kStages = 3;
-  constexpr int kOnes = kStages * TB::STAGE;   // 1 KB of E4M3 1.0: the row-sum MFMA operand
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * TB::STAGE + 1024];
+  constexpr int kStages = 4;
+  constexpr int kOnes = kStages * TB::REC;   // 1 KB of E4M3 1.0: the row-sum MFMA operand
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * TB::REC + 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,10 +335,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int row_lim = (CAUSAL ? min(a.seq_k - 1, row + off) : a.seq_k - 1) - 16 * lh;
 
   const int64_t bk = (int64_t)b * a.kv_heads + kvh;
-  const uint8_t* gk = a.wk + bk * a.n_tiles * TB::K;
-  const uint8_t* gks = a.wks + bk * a.n_tiles * TB::KS;
-  const uint8_t* gv = a.wv + bk * a.n_tiles * TB::V;
-  const uint32_t* gvs = a.wvs + bk * a.n_tiles;
+  const uint8_t* const grec = a.rec + bk * a.n_tiles * TB::REC + lane * 16;
 
   // ---- Q prologue: this wave's 32 rows to MXFP4 in registers; lane (q, h)
   // holds head_dim block 2s + h of row q for contraction step s ----
@@ -334,79 +377,97 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const bool row_live = row < a.seq_q;
   const float cexp = a.c;
 
-  // ---- tile staging: global -> registers -> LDS.  The staging arrays are
-  // clang vectors indexed only at compile time, so they stay in VGPRs. ----
-  constexpr int KV4 = TB::K / 16, VV4 = TB::V / 16, KSV4 = TB::KS / 16;
-  constexpr int KPT = (KV4 + kThreads - 1) / kThreads, VPT = (VV4 + kThreads - 1) / kThreads;
-  v4i rk[KPT], rv[VPT], rks;
-  uint32_t rvs = 0;
-  auto gload = [&](int tile) __attribute__((always_inline)) {
-    const v4i* sk = reinterpret_cast<const v4i*>(gk + (int64_t)tile * TB::K);
-    const v4i* sv = reinterpret_cast<const v4i*>(gv + (int64_t)tile * TB::V);
-    static_for<KPT>([&](auto I) {
+  // ---- tile staging: direct global->LDS loads of 1 KB chunks; wave w
+  // copies chunks w, w+8, ... of each tile record ----
+  const int my_chunks = (TB::CHUNKS - wave + kWaves - 1) / kWaves;
+  auto dma = [&](int tile) __attribute__((always_inline)) {
+    const uint8_t* src = grec + (int64_t)tile * TB::REC;
+    uint8_t* dst = lds + (tile % kStages) * TB::REC;
+    static_for<(TB::CHUNKS + kWaves - 1) / kWaves>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      if (KV4 % kThreads == 0 || tid + i * kThreads < KV4) rk[i] = sk[tid + i * kThreads];
+      const int c = wave + kWaves * i;
+      if (kWaves * (i + 1) <= TB::CHUNKS || c < TB::CHUNKS) global_to_lds16(src + c * 1024, dst + c * 1024);
     });
-    static_for<VPT>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      if (VV4 % kThreads == 0 || tid + i * kThreads < VV4) rv[i] = sv[tid + i * kThreads];
-    });
-    if (tid < KSV4) rks = reinterpret_cast<const v4i*>(gks + (int64_t)tile * TB::KS)[tid];
-    if (tid == 0) rvs = gvs[tile];
   };
-  auto sstore = [&](int stage) __attribute__((always_inline)) {
-    uint8_t* base = lds + stage * TB::STAGE;
-    static_for<KPT>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      if (KV4 % kThreads == 0 || tid + i * kThreads < KV4) reinterpret_cast<v4i*>(base)[tid + i * kThreads] = rk[i];
-    });
-    static_for<VPT>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      if (VV4 % kThreads == 0 || tid + i * kThreads < VV4)
-        reinterpret_cast<v4i*>(base + TB::K + TB::KS)[tid + i * kThreads] = rv[i];
-    });
-    if (tid < KSV4) reinterpret_cast<v4i*>(base + TB::K)[tid] = rks;
-    if (tid == 0) *reinterpret_cast<uint32_t*>(base + TB::K + TB::KS + TB::V) = rvs;
+  // wait until at most `pending` of this wave's direct loads are in flight
+  auto wait_dma = [&](int pending) __attribute__((always_inline)) {
+    switch (pending) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1>(); break;
+      case 2: wait_vmcnt<2>(); break;
+      case 3: wait_vmcnt<3>(); break;
+      default: wait_vmcnt<4>(); break;
+    }
   };
 
   // MFMA step k: O^T += V^T·P^T and L += 1·P^T for tile k-1 (FP8 x FP8),
   // then S^T = K·Q^T for tile k (FP4 x FP4; both operands' E8M0 scales are
   // applied inside the instruction, so the scores come out dequantized).
-  auto mfma_step = [&](int k) __attribute__((always_inline)) {
+  // LDS reads are software-pipelined against the matrix instructions: the V
+  // operands of head_dim block db+1 are read while the four P·V instructions
+  // of block db run, and the K operands of the QK^T while the row sums run,
+  // so no LDS round trip sits between two matrix instructions.  (The four instructions of a block accumulate into one
+  // register block back to back, which the matrix core chains directly.)
+  auto mfma_step = [&](int k, auto with_pv, auto with_qk) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(with_pv)::value, QK = decltype(with_qk)::value;
     __builtin_amdgcn_s_setprio(1);
-    if (k >= 1) {
-      const uint8_t* base = lds + ((k - 1) % kStages) * TB::STAGE;
-      const uint8_t* lv = base + TB::K + TB::KS;
-      const uint32_t vsw = *reinterpret_cast<const uint32_t*>(base + TB::K + TB::KS + TB::V);
-      const v4i o0 = *reinterpret_cast<const v4i*>(lds + kOnes + (lane & 31) * 16);
-      const v8i ones = __builtin_shufflevector(o0, o0, 0, 1, 2, 3, 0, 1, 2, 3);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int vsc = (int)((vsw >> (8 * (2 * s2 + lh))) & 0xFF);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const uint8_t* src = lv + (db * 2 + s2) * 2048 + lane * 16;
-          const v4i v0 = *reinterpret_cast<const v4i*>(src);
-          const v4i v1 = *reinterpret_cast<const v4i*>(src + 1024);
-          const v8i av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          O[db] = mfma32x32x64<kFmtFp8, kFmtFp8>(av, Phi[s2], O[db], vsc, psc);
-          O[db] = mfma32x32x64<kFmtFp8, kFmtFp8>(av, Plo[s2], O[db], vsc, psc - 4);
-        }
-        L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[s2], L, 127, psc);
-        L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[s2], L, 127, psc - 4);
-      }
-    }
-    if (k < nt) {
-      const uint8_t* base = lds + (k % kStages) * TB::STAGE;
+    v4i kf[4 * NS];
+    uint32_t ks[NS];
+    auto kload = [&]() __attribute__((always_inline)) {
+      const uint8_t* base = lds + (k % kStages) * TB::REC;
+      static_for<4 * NS>([&](auto I) {
+        constexpr int idx = decltype(I)::value;
+        kf[idx] = *reinterpret_cast<const v4i*>(base + (idx * 64 + lane) * 16);
+      });
       const uint32_t* ksw = reinterpret_cast<const uint32_t*>(base + TB::K + lane * (4 * NS));
-      uint32_t ks[NS];
 #pragma unroll
       for (int i = 0; i < NS; ++i) ks[i] = ksw[i];
+    };
+    if constexpr (PV) {
+      const uint8_t* base = lds + ((k - 1) % kStages) * TB::REC;
+      const uint8_t* lv = base + TB::K + TB::SC + lane * 16;
+      const uint32_t vsw = *reinterpret_cast<const uint32_t*>(base + TB::K + TB::VS_OFF);
+      const v4i o0 = *reinterpret_cast<const v4i*>(lds + kOnes + (lane & 31) * 16);
+      const v8i ones = __builtin_shufflevector(o0, o0, 0, 1, 2, 3, 0, 1, 2, 3);
+      const int vsc0 = (int)((vsw >> (8 * lh)) & 0xFF), vsc1 = (int)((vsw >> (8 * (2 + lh))) & 0xFF);
+      // head_dim block db: operands for both 64-key halves, read one block ahead
+      v8i av[2][2];
+      auto vload = [&](auto DB) __attribute__((always_inline)) {
+        constexpr int db = decltype(DB)::value;
+        static_for<2>([&](auto S2) {
+          constexpr int s2 = decltype(S2)::value;
+          const v4i v0 = *reinterpret_cast<const v4i*>(lv + (db * 2 + s2) * 2048);
+          const v4i v1 = *reinterpret_cast<const v4i*>(lv + (db * 2 + s2) * 2048 + 1024);
+          av[db & 1][s2] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        });
+      };
+      vload(std::integral_constant<int, 0>{});
+      static_for<NDB + 1>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if constexpr (j < NDB - 1) vload(std::integral_constant<int, j + 1>{});
+        if constexpr (j == NDB && QK) kload();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j < NDB) {
+          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][0], Phi[0], O[j], vsc0, psc);
+          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][0], Plo[0], O[j], vsc0, psc - 4);
+          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][1], Phi[1], O[j], vsc1, psc);
+          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][1], Plo[1], O[j], vsc1, psc - 4);
+        } else {
+          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[0], L, 127, psc);
+          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[0], L, 127, psc - 4);
+          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[1], L, 127, psc);
+          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[1], L, 127, psc - 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else if constexpr (QK) {
+      kload();
+    }
+    if constexpr (QK) {
       static_for<4 * NS>([&](auto I) {
-        constexpr int idx = decltype(I)::value;           // kb * NS + st
-        constexpr int kb = idx / NS, st = idx % NS;
-        const v8i af = fp4_operand(*reinterpret_cast<const uint4*>(base + (idx * 64 + lane) * 16));
-        S[kb] = mfma32x32x64<kFmtFp4, kFmtFp4, idx & 3, 0>(af, qf[st], st == 0 ? v16f{} : S[kb],
+        constexpr int st = decltype(I)::value / 4, kb = decltype(I)::value % 4;
+        constexpr int idx = kb * NS + st;
+        S[kb] = mfma32x32x64<kFmtFp4, kFmtFp4, idx & 3, 0>(fp4_operand(kf[idx]), qf[st], st == 0 ? v16f{} : S[kb],
                                                           (int)ks[idx >> 2], qsc[st]);
       });
     }
@@ -415,7 +476,6 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // VALU step k: mask, online softmax and two-term FP8 split of tile k.
   auto valu_step = [&](int k) __attribute__((always_inline)) {
-    if (k < 0 || k >= nt) return;
     if (k * kKvTile + kKvTile - 1 > mask_lim) {      // tiles crossing the diagonal or seq_k
       // element i of key block kb in this lane is key 32*kb + 16*h + i
       const int lim = row_lim - k * kKvTile;
@@ -427,21 +487,48 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     softmax_tile32<NDB>(S, cexp, m_run, O, L, Phi, Plo, psc);
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  if (grp == 1) __syncthreads();       // group 1 runs one phase behind
-  for (int k = 0; k <= nt; ++k) {
-    const bool next = k + 1 < nt;
-    if (next) gload(k + 1);
-    mfma_step(k);
-    if (grp == 1 && next) sstore((k + 1) % kStages);
-    __syncthreads();
-    valu_step(k);
-    if (grp == 0 && next) sstore((k + 1) % kStages);
-    __syncthreads();
-  }
-  if (grp == 0) __syncthreads();       // matches group 1's initial wait
+  // one iteration of the schedule for tile k; the first (no P·V yet) and the
+  // final P·V-only step are peeled so the steady state has no branches
+  auto iteration = [&](int k, auto with_pv, auto with_qk) __attribute__((always_inline)) {
+    const bool prefetch = k + 2 < nt;
+    if (prefetch) dma(k + 2);
+    // tile k+1 must have landed (from this wave) before the barrier that ends
+    // phase 2k+1: group 1's MFMA phase, group 0's VALU phase
+    const int pending = prefetch ? my_chunks : 0;
+    mfma_step(k, with_pv, with_qk);
+    // The matrix instructions are pure values to the compiler, which would
+    // otherwise sink them past the barrier into the other phase: an empty asm
+    // that reads the accumulators keeps them (and the softmax below) on their
+    // side of it.
+    if constexpr (decltype(with_pv)::value) {
+      static_for<NDB>([&](auto DB) { keep_in_vgprs(O[decltype(DB)::value]); });
+      keep_in_vgprs(L);
+    }
+    if constexpr (decltype(with_qk)::value) {
+      static_for<4>([&](auto KB) { keep_in_vgprs(S[decltype(KB)::value]); });
+    }
+    if (grp == 1 && k + 1 < nt) wait_dma(pending);
+    phase_barrier();
+    if constexpr (decltype(with_qk)::value) {
+      valu_step(k);
+      static_for<2>([&](auto I) {
+        keep_in_vgprs(Phi[decltype(I)::value]);
+        keep_in_vgprs(Plo[decltype(I)::value]);
+      });
+    }
+    if (grp == 0 && k + 1 < nt) wait_dma(pending);
+    phase_barrier();
+  };
+  dma(0);
+  if (nt > 1) dma(1);
+  wait_dma(nt > 1 ? my_chunks : 0);    // tile 0 (this wave's chunks)
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the ones operand is written
+  phase_barrier();
+  if (grp == 1) phase_barrier();       // group 1 runs one phase behind
+  iteration(0, std::false_type{}, std::true_type{});
+  for (int k = 1; k < nt; ++k) iteration(k, std::true_type{}, std::true_type{});
+  iteration(nt, std::true_type{}, std::false_type{});
+  if (grp == 0) phase_barrier();       // matches group 1's initial wait
 
   // ---- epilogue: normalize by the sum of the quantized weights, store bf16
   // rows and the log-sum-exp.  Element i of head_dim block db in lane (q, h)
@@ -475,13 +562,12 @@ static hipError_t launch_pack_d(const PrefillParams& p, hipStream_t stream) {
   const int64_t bk = (int64_t)p.batch * p.kv_heads;
   const int64_t total_k = bk * L.n_tiles * kKvTile * (D / 32);
   hipLaunchKernelGGL((pack_k_kernel<D>), dim3((unsigned)((total_k + 255) / 256)), dim3(256), 0, stream, p.k,
-                     p.ks[0], p.ks[1], p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, p.ws + L.off_k, p.ws + L.off_ks,
-                     total_k);
+                     p.ks[0], p.ks[1], p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, p.ws + L.off_rec, total_k);
   hipLaunchKernelGGL((vtile_scale_kernel<D>), dim3((unsigned)(bk * L.n_vtiles)), dim3(256), 0, stream, p.v,
                      p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_vtiles, wvt);
   hipLaunchKernelGGL((pack_v_kernel<D>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v, p.vs[0],
                      p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_tiles, L.n_vtiles, wvt,
-                     p.ws + L.off_v, reinterpret_cast<uint32_t*>(p.ws + L.off_vs));
+                     p.ws + L.off_rec);
   return hipGetLastError();
 }
 
@@ -490,8 +576,7 @@ static hipError_t launch_attn_d(const PrefillParams& p, hipStream_t stream) {
   const PrefillLayout L = prefill_layout(p.batch, p.kv_heads, p.seq_k, D, p.v_tile_rows);
   AttnArgs a;
   a.q = p.q; a.o = p.o; a.lse = p.lse;
-  a.wk = p.ws + L.off_k; a.wks = p.ws + L.off_ks; a.wv = p.ws + L.off_v;
-  a.wvs = reinterpret_cast<const uint32_t*>(p.ws + L.off_vs);
+  a.rec = p.ws + L.off_rec;
   a.qs0 = p.qs[0]; a.qs1 = p.qs[1]; a.qs2 = p.qs[2];
   a.os0 = p.os[0]; a.os1 = p.os[1]; a.os2 = p.os[2];
   a.q_heads = p.q_heads; a.kv_heads = p.kv_heads;

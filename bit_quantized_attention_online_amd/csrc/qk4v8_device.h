@@ -46,9 +46,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // An FP4 MFMA operand: 16 bytes of E2M1 codes in the low half of the 8-dword
 // operand; the upper half is left undefined so the backend passes 4 VGPRs.
-__device__ __forceinline__ v8i fp4_operand(uint4 x) {
-  const v4i v = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+__device__ __forceinline__ v8i fp4_operand(v4i v) {
   return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+__device__ __forceinline__ v8i fp4_operand(uint4 x) {
+  return fp4_operand(v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w});
 }
 
 constexpr int kFmtFp8 = 0;   // E4M3 operand format code of the scaled MFMA
@@ -196,18 +198,38 @@ __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run,
   }
 }
 
+// Maximum over the two lanes l and l^32 (v_permlane32_swap exchanges the
+// halves of the wave without an LDS round trip; max is symmetric, so the pair
+// of results gives the partner's value whichever way round they come).
+__device__ __forceinline__ float max_with_lane_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // The same step for the 32x32x64 layout: S holds the 4 key-block results of
 // this lane (64 scores of query lane%32, split with lane^32), P byte j of the
 // 8-dword operand of P·V step s2 holds key-block 2*s2 + j/16, element j%16.
+// One wave runs this alone on its SIMD while the other feeds the matrix core,
+// so it is written as independent passes over all 64 scores (in place in S):
+// the exponentials, then the hi codes, then the residuals, then the lo codes,
+// which lets the scheduler hide the latency of the transcendental and convert
+// instructions behind independent work.
 template <int NO>
 __device__ __forceinline__ void softmax_tile32(v16f (&S)[4], float c, float& m_run, v16f (&O)[NO], v16f& L,
                                                v8i (&Phi)[2], v8i (&Plo)[2], int& psc) {
-  float mx = S[0][0];
+  // row maximum: four independent chains, then a tree
+  float m4[4];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < 4; ++kb) {
+    float a = fmaxf(S[kb][0], S[kb][1]), b = fmaxf(S[kb][2], S[kb][3]);
 #pragma unroll
-    for (int i = (kb == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, S[kb][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    for (int i = 4; i < 16; i += 4) {
+      a = fmaxf(a, fmaxf(S[kb][i], S[kb][i + 1]));
+      b = fmaxf(b, fmaxf(S[kb][i + 2], S[kb][i + 3]));
+    }
+    m4[kb] = fmaxf(a, b);
+  }
+  const float mx = max_with_lane_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
   const float tmax = mx * c;
   const float m_new = fmaxf(m_run, tmax);
   const bool grow = __builtin_amdgcn_readfirstlane((int)__any(m_new > m_run + kLazyRescale)) != 0;
@@ -222,24 +244,42 @@ __device__ __forceinline__ void softmax_tile32(v16f (&S)[4], float c, float& m_r
   const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
   psc = X + 127;
   const float sh = exp2i(X), sl = exp2i(X - 4);
+  // p = 2^(s*c - m), in place
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[kb][i] = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -m_use));
+  // hi = E4M3(p / 2^X)
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(S[kb][4 * w + e], c, -m_use));
       const int dw = 4 * (kb & 1) + w;
-      uint32_t h = e4m3_put2<false>((uint32_t)Phi[kb >> 1][dw], p[0], p[1], sh);
-      h = e4m3_put2<true>(h, p[2], p[3], sh);
+      uint32_t h = e4m3_put2<false>((uint32_t)Phi[kb >> 1][dw], S[kb][4 * w], S[kb][4 * w + 1], sh);
+      Phi[kb >> 1][dw] = (int)e4m3_put2<true>(h, S[kb][4 * w + 2], S[kb][4 * w + 3], sh);
+    }
+  // residual p - hi * 2^X, in place
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t h = (uint32_t)Phi[kb >> 1][4 * (kb & 1) + w];
       const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, false);
       const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, true);
-      uint32_t l = e4m3_put2<false>((uint32_t)Plo[kb >> 1][dw], p[0] - b01[0], p[1] - b01[1], sl);
-      l = e4m3_put2<true>(l, p[2] - b23[0], p[3] - b23[1], sl);
-      Phi[kb >> 1][dw] = (int)h;
-      Plo[kb >> 1][dw] = (int)l;
+      S[kb][4 * w] -= b01[0];
+      S[kb][4 * w + 1] -= b01[1];
+      S[kb][4 * w + 2] -= b23[0];
+      S[kb][4 * w + 3] -= b23[1];
     }
-  }
+  // lo = E4M3(residual / 2^(X-4))
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int dw = 4 * (kb & 1) + w;
+      uint32_t l = e4m3_put2<false>((uint32_t)Plo[kb >> 1][dw], S[kb][4 * w], S[kb][4 * w + 1], sl);
+      Plo[kb >> 1][dw] = (int)e4m3_put2<true>(l, S[kb][4 * w + 2], S[kb][4 * w + 3], sl);
+    }
 }
 
 __device__ __forceinline__ float wave_max(float v) {

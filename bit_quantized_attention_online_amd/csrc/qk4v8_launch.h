@@ -20,7 +20,8 @@ hipError_t launch_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int d
 struct PrefillLayout {
   int64_t n_tiles;        // ceil(seq_k / 128)
   int64_t n_vtiles;       // ceil(seq_k / v_tile_rows)
-  size_t off_k, off_ks, off_v, off_vs, off_vtile, total;
+  int64_t rec_bytes;      // one packed K/V tile record
+  size_t off_rec, off_vtile, total;
 };
 PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, int v_tile_rows);
 
