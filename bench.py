@@ -7,7 +7,8 @@ pre-pass plus the attention kernel, which quantizes Q in its prologue.  The
 decode (batch 64, 64/8 heads, 32768 cached tokens) and block-verify (batch 32,
 8 queries over 16384 + 8 cached tokens) workloads are timed in the same run and
 reported as extra objects.  Inputs are seeded and synthetic and resident in HBM
-before timing starts.
+before timing starts; each workload first runs untimed for half a second so
+that the GPU's clocks settle, then W warmup steps, then K timed steps.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -29,6 +30,7 @@ PEAK_FP8_TFLOPS = 5000.0       # dense FP8 MFMA
 # QK^T runs on FP4 and P·V on FP8 with equal algorithmic flops, so the time
 # floor is F/2/P_fp4 + F/2/P_fp8, i.e. the harmonic mean of the two peaks.
 PEAK_MIXED_TFLOPS = 2.0 / (1.0 / PEAK_FP4_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
+SETTLE_S = 0.5                 # untimed sustained load before the warmup steps
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_causal_gqa_n4096_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "bit_quantized_attention_online_amd", "csrc", "prefill.hip")
 
@@ -60,6 +62,18 @@ class Events:
         return self.ev[i].elapsed_time(self.ev[j])
 
 
+def settle(torch, step, seconds=SETTLE_S):
+    """Run the workload untimed for a fixed wall time before the warmup steps:
+    the GPU takes tens of milliseconds of sustained load to reach its steady
+    clocks, longer than a few warmup steps last."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+
+
 def bench_prefill(torch, ops, synth, steps, warmup):
     w = synth.WORKLOADS[2]
     log("[bench] generating the causal GQA prefill workload")
@@ -71,6 +85,7 @@ def bench_prefill(torch, ops, synth, steps, warmup):
     pp = ops.PackedPrefill(qd, kd, vd, causal=True, softmax_scale=1.0 / math.sqrt(w["d"]),
                            v_tile_rows=w["v_tile_rows"])
     stream = torch.cuda.current_stream()
+    settle(torch, lambda: (pp.pack(), pp.attend()))
     for _ in range(warmup):
         pp.pack()
         pp.attend()
@@ -128,6 +143,7 @@ def bench_decode(torch, ops, synth, cfg, steps, warmup):
                      device=q.device)
     run = lambda: ops.attn_decode(q, kc, ks, vc, vs, w["kv_len"], v_tile_rows=w["v_tile_rows"], out=o, workspace=ws,
                                   softmax_scale=1.0 / math.sqrt(w["d"]))
+    settle(torch, run)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -186,8 +202,8 @@ def calib_copy(torch, nbytes=1 << 30):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
