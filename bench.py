@@ -161,11 +161,66 @@ def bench_decode(torch, ops, synth, cfg, steps, warmup):
     kv_bytes = w["B"] * w["Hkv"] * (w["kv_len"] * per_token + -(-w["kv_len"] // w["v_tile_rows"]))
     qo_bytes = 2 * (w["B"] * w["q_len"] * w["Hq"] * d * 2)
     gbs = (kv_bytes + qo_bytes) / (ms * 1e-3) / 1e9
+    out = dict(workload=w["name"], value=round(gbs, 1), unit="GB/s", ms=round(ms, 4),
+               bytes=kv_bytes + qo_bytes,
+               roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                             frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+    # the cache writer of the same step: q_len new tokens per sequence appended
+    # at the end of the cache (the last q_len positions are rewritten)
+    out["kv_append"] = bench_append(torch, ops, kc, ks, vc, vs, w["B"], w["Hkv"], d, w["q_len"],
+                                    w["kv_len"] - w["q_len"], w["v_tile_rows"], steps, warmup, seed=2000 + cfg)
     del kc, ks, vc, vs
-    return dict(workload=w["name"], value=round(gbs, 1), unit="GB/s", ms=round(ms, 4),
-                bytes=kv_bytes + qo_bytes,
+    return out
+
+
+def bench_append(torch, ops, kc, ks, vc, vs, B, Hkv, d, n_new, kv_len, R, steps, warmup, seed):
+    """Time qk4v8_kv_append of n_new tokens per sequence at position kv_len.
+    Algorithmic bytes per (token, kv-head): K and V read as bf16 (4d), K codes
+    and scales plus V codes written (d/2 + d/32 + d), and the V row copied to the
+    tail buffer when it lands in a partial tile (2d)."""
+    dev = kc.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    kn = torch.randn((B, n_new, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((B, n_new, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    tail = torch.zeros((B, Hkv, R, d), dtype=torch.bfloat16, device=dev)
+    run = lambda: ops.kv_append(kn, vn, kc, ks, vc, vs, tail, kv_len, v_tile_rows=R)
+    settle(torch, run, seconds=0.1)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [Events(torch, 2) for _ in range(steps)]
+    for e in evs:
+        e.record(0, stream)
+        run()
+        e.record(1, stream)
+    torch.cuda.synchronize()
+    ms = sum(e.ms(0, 1) for e in evs) / steps
+    end = kv_len + n_new
+    tail_rows = end - max(kv_len, (end // R) * R)
+    nbytes = B * Hkv * (n_new * (4 * d + d // 2 + d // 32 + d) + tail_rows * 2 * d)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(tokens_per_sequence=n_new, batch=B, kv_heads=Hkv, position=kv_len, us=round(ms * 1e3, 2),
+                value=round(gbs, 1), unit="GB/s", bytes=nbytes,
                 roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                               frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+
+
+def bench_append_prefill(torch, ops, synth, steps, warmup):
+    """Cache ingestion of a whole prompt: the causal GQA workload's K/V (4096
+    tokens per sequence) appended into an empty cache in one call."""
+    w = synth.WORKLOADS[2]
+    B, Hkv, d, n = w["B"], w["Hkv"], w["d"], w["Nk"]
+    R = 256
+    dev = torch.device("cuda:0")
+    kc = torch.zeros((B, Hkv, n, d // 2), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((B, Hkv, n, d // 32), dtype=torch.uint8, device=dev)
+    vc = torch.zeros((B, Hkv, n, d), dtype=torch.uint8, device=dev)
+    vs = torch.zeros((B, Hkv, -(-n // R)), dtype=torch.uint8, device=dev)
+    out = bench_append(torch, ops, kc, ks, vc, vs, B, Hkv, d, n, 0, R, steps, warmup, seed=3000)
+    out["workload"] = f"cache_ingest_b{B}_hkv{Hkv}_n{n}_d{d}_r{R}"
+    return out
 
 
 def cpu_baseline(synth):
@@ -256,6 +311,8 @@ def main():
         line["decode"] = bench_decode(torch, ops, synth, 3, args.steps, args.warmup)
         torch.cuda.empty_cache()
         line["block_verify"] = bench_decode(torch, ops, synth, 5, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        line["kv_append_prompt"] = bench_append_prefill(torch, ops, synth, args.steps, args.warmup)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")

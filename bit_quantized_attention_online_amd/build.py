@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqk4v8.so")
-SOURCES = ["qk4v8_api.hip", "quantize.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["qk4v8_api.hip", "quantize.hip", "prefill.hip", "decode.hip", "append.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,163 @@
+// KV-cache append: new tokens' K rows to MXFP4 and V rows to per-tile FP8,
+// written into the cache layout the decode kernel reads.
+//
+// "MpFA免训练量化：QK4V8混合精度在Blackwell上的推理加速实践" §6.1: the KV cache is
+// kept quantized, so every new token is quantized when it is written; §3.2:
+// each block's scale comes from the block itself.  For V the block is a tile of
+// R rows of one (batch, kv-head), so the last tile of a sequence keeps growing
+// as tokens arrive and its scale must always be that of all the rows it holds.
+// E8M0 scales are monotone in the absolute maximum, so the new scale of a
+// filling tile is max(old, scale of the new rows): when it does not change,
+// only the new rows are encoded (their codes are the same as a full
+// re-quantization would give); when it grows, the tile is re-quantized from
+// the bf16 rows the caller's tail buffer keeps for the partial tile.
+//
+// Three launches on the caller's stream:
+//   append_k_kernel     thread per (b, token, kv-head, 32-element block)
+//   append_v_kernel     workgroup per (b, kv-head, tile touched by the append)
+//   append_tail_kernel  copies the new rows of each new partial tile into the
+//                       tail buffer (after append_v_kernel has read it)
+#include "qk4v8_device.h"
+#include "qk4v8_launch.h"
+
+namespace qk4v8 {
+
+namespace {
+
+// Cache length of sequence b, or -1 when the append does not fit.
+__device__ __forceinline__ int append_len(const AppendParams& p, int b) {
+  const int len = p.kv_lens ? p.kv_lens[b] : p.kv_len;
+  return (len < 0 || (int64_t)len + p.n_new > p.cap) ? -1 : len;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) append_k_kernel(AppendParams p, int64_t total) {
+  constexpr int NB = D / 32;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= total) return;
+  const int g = (int)(id % NB);
+  const int64_t rest = id / NB;
+  const int h = (int)(rest % p.kv_heads);
+  const int64_t bt = rest / p.kv_heads;
+  const int t = (int)(bt % p.n_new);
+  const int b = (int)(bt / p.n_new);
+  const int len = append_len(p, b);
+  if (len < 0) return;
+  const uint4* src = reinterpret_cast<const uint4*>(p.k_new + b * p.ks[0] + t * p.ks[1] + h * p.ks[2] + 32 * g);
+  uint32_t w[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 x = src[q];
+    w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
+  }
+  uint32_t codes[4];
+  const uint32_t scale = mxfp4_quantize32(w, codes);
+  const int64_t row = ((int64_t)b * p.kv_heads + h) * p.cap + len + t;
+  *reinterpret_cast<uint4*>(p.k_codes + row * (D / 2) + 16 * g) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+  p.k_scales[row * NB + g] = (uint8_t)scale;
+}
+
+// Workgroup per (b, h, slot): slot s handles tile floor(len/R) + s.  Rows of
+// the tile in [len, end) are new (from v_new); rows in [tile*R, len) were
+// cached earlier and their bf16 values are in the tail buffer.
+template <int D>
+__global__ void __launch_bounds__(256) append_v_kernel(AppendParams p, int slots) {
+  constexpr int CPR = D / 8;                        // 16-byte chunks per row
+  __shared__ float red[4];
+  const int slot = (int)(blockIdx.x % slots);
+  const int64_t bh = blockIdx.x / slots;
+  const int b = (int)(bh / p.kv_heads), h = (int)(bh - (int64_t)b * p.kv_heads);
+  const int len = append_len(p, b);
+  if (len < 0) return;
+  const int R = p.R;
+  const int end = len + p.n_new;
+  const int tile = len / R + slot;
+  const int r0 = tile * R;
+  if (r0 >= end) return;                            // uniform across the workgroup
+  const int r1 = min(r0 + R, end);
+  const int first_new = max(r0, len);
+  // absolute maximum of the new rows of this tile
+  float amax = 0.0f;
+  const int nvec_new = (r1 - first_new) * CPR;
+  for (int vi = threadIdx.x; vi < nvec_new; vi += 256) {
+    const int r = first_new + vi / CPR, cc = vi % CPR;
+    const uint4 w = *reinterpret_cast<const uint4*>(p.v_new + b * p.vs[0] + (int64_t)(r - len) * p.vs[1] +
+                                                    h * p.vs[2] + cc * 8);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(ws[k])), fabsf(bf16_hi(ws[k]))));
+  }
+  amax = block_max256(amax, red);
+  uint8_t* const scale_ptr = p.v_scales + bh * p.n_vtiles_cap + tile;
+  const bool has_old = len > r0;                    // the tile was partly filled before
+  int X = mx_shared_exp(amax, 8);
+  const int X_old = has_old ? (int)*scale_ptr - 127 : -127;
+  const bool requant = has_old && X > X_old;
+  X = max(X, X_old);
+  const float inv = exp2i(-X);
+  uint8_t* const codes = p.v_codes + (bh * p.cap) * D;
+  // re-encode the earlier rows from their bf16 values when the scale grew
+  if (requant) {
+    const uint16_t* tail = p.v_tail + bh * R * D;
+    const int nvec_old = (len - r0) * CPR;
+    for (int vi = threadIdx.x; vi < nvec_old; vi += 256) {
+      const int i = vi / CPR, cc = vi % CPR;
+      const uint4 w = *reinterpret_cast<const uint4*>(tail + (int64_t)i * D + cc * 8);
+      *reinterpret_cast<uint2*>(codes + (int64_t)(r0 + i) * D + cc * 8) = e4m3_quantize8(w, inv);
+    }
+  }
+  for (int vi = threadIdx.x; vi < nvec_new; vi += 256) {
+    const int r = first_new + vi / CPR, cc = vi % CPR;
+    const uint4 w = *reinterpret_cast<const uint4*>(p.v_new + b * p.vs[0] + (int64_t)(r - len) * p.vs[1] +
+                                                    h * p.vs[2] + cc * 8);
+    *reinterpret_cast<uint2*>(codes + (int64_t)r * D + cc * 8) = e4m3_quantize8(w, inv);
+  }
+  if (threadIdx.x == 0) *scale_ptr = (uint8_t)(X + 127);
+}
+
+// Thread per (b, h, tail row, 16-byte chunk): rows of the new last partial tile
+// that arrived in this call are copied into the tail buffer.
+template <int D>
+__global__ void __launch_bounds__(256) append_tail_kernel(AppendParams p, int64_t total) {
+  constexpr int CPR = D / 8;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= total) return;
+  const int cc = (int)(id % CPR);
+  const int i = (int)((id / CPR) % p.R);
+  const int64_t bh = id / ((int64_t)CPR * p.R);
+  const int b = (int)(bh / p.kv_heads), h = (int)(bh - (int64_t)b * p.kv_heads);
+  const int len = append_len(p, b);
+  if (len < 0) return;
+  const int end = len + p.n_new;
+  const int r = (end / p.R) * p.R + i;              // row i of the last tile
+  if (r >= end || r < len) return;                  // absent, or already in the tail
+  const uint4 w = *reinterpret_cast<const uint4*>(p.v_new + b * p.vs[0] + (int64_t)(r - len) * p.vs[1] +
+                                                  h * p.vs[2] + cc * 8);
+  *reinterpret_cast<uint4*>(p.v_tail + (bh * p.R + i) * D + cc * 8) = w;
+}
+
+}  // namespace
+
+template <int D>
+static hipError_t launch_append_d(const AppendParams& p, hipStream_t stream) {
+  const int64_t bh = (int64_t)p.batch * p.kv_heads;
+  const int64_t total_k = bh * p.n_new * (D / 32);
+  hipLaunchKernelGGL((append_k_kernel<D>), dim3((unsigned)((total_k + 255) / 256)), dim3(256), 0, stream, p, total_k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // tiles touched per sequence: at most ceil(n_new / R) + 1
+  const int slots = (p.n_new + p.R - 1) / p.R + 1;
+  hipLaunchKernelGGL((append_v_kernel<D>), dim3((unsigned)(bh * slots)), dim3(256), 0, stream, p, slots);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total_t = bh * p.R * (D / 8);
+  hipLaunchKernelGGL((append_tail_kernel<D>), dim3((unsigned)((total_t + 255) / 256)), dim3(256), 0, stream, p,
+                     total_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
+  return p.head_dim == 64 ? launch_append_d<64>(p, stream) : launch_append_d<128>(p, stream);
+}
+
+}  // namespace qk4v8

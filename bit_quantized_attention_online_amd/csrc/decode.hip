@@ -141,12 +141,17 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
         rk[i] = *reinterpret_cast<const v4i*>(gk + (int64_t)key * (D / 2) + (ci % NB) * 16);
       }
     });
+    // V rows past the sequence's length are zeroed: their weights are 0 after
+    // the mask, but cache bytes there may be anything (E4M3 NaN included), and
+    // 0 * NaN would reach the accumulator
     static_for<VPT>([&](auto I) {
       constexpr int i = decltype(I)::value;
       const int ci = tid + i * NT;
       if (VCH % NT == 0 || ci < VCH) {
-        const int key = min(j0_ + ci / NC, a.cap - 1);
+        const int j = j0_ + ci / NC;
+        const int key = min(j, a.cap - 1);
         rv[i] = *reinterpret_cast<const v4i*>(gv + (int64_t)key * D + (ci % NC) * 16);
+        if (j >= kvlen) rv[i] = v4i{0, 0, 0, 0};
       }
     });
     static_for<SPT>([&](auto I) {

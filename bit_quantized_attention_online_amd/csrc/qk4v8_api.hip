@@ -212,6 +212,40 @@ size_t qk4v8_decode_workspace_bytes(const qk4v8_decode_args* a) {
   return decode_workspace_bytes(a->batch, a->q_len, a->q_heads, a->kv_heads, a->head_dim, decode_splits(a));
 }
 
+qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream) {
+  if (a == nullptr) return QK4V8_ERR_NULL;
+  if (a->batch < 0 || a->kv_heads < 1 || a->n_new < 0 || a->cap < 0) return QK4V8_ERR_SHAPE;
+  if (a->head_dim != 64 && a->head_dim != 128) return QK4V8_ERR_SHAPE;
+  if (!valid_v_tile(a->v_tile_rows)) return QK4V8_ERR_SHAPE;
+  if (a->kv_lens == nullptr && (a->kv_len < 0 || (int64_t)a->kv_len + a->n_new > a->cap)) return QK4V8_ERR_SHAPE;
+  if (a->cap > (1 << 30)) return QK4V8_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if (a->k_stride[i] < 0 || a->k_stride[i] % 8 != 0 || a->v_stride[i] < 0 || a->v_stride[i] % 8 != 0)
+      return QK4V8_ERR_STRIDE;
+  if (a->batch == 0 || a->n_new == 0) return QK4V8_OK;
+  if (!a->k_new || !a->v_new || !a->k_codes || !a->k_scales || !a->v_codes || !a->v_scales || !a->v_tail)
+    return QK4V8_ERR_NULL;
+  if (!aligned(a->k_new, 16) || !aligned(a->v_new, 16) || !aligned(a->v_tail, 16) || !aligned(a->k_codes, 16) ||
+      !aligned(a->v_codes, 8))
+    return QK4V8_ERR_STRIDE;
+  if (a->kv_lens && !aligned(a->kv_lens, 4)) return QK4V8_ERR_STRIDE;
+  const int64_t bh = (int64_t)a->batch * a->kv_heads;
+  if (bh * ((a->n_new + a->v_tile_rows - 1) / a->v_tile_rows + 1) > 0x7FFFFFFF ||
+      (bh * a->n_new * (a->head_dim / 32) + 255) / 256 > 0x7FFFFFFF)
+    return QK4V8_ERR_SHAPE;
+  qk4v8_status st = check_device();
+  if (st != QK4V8_OK) return st;
+  AppendParams p;
+  p.k_new = a->k_new; p.v_new = a->v_new;
+  for (int i = 0; i < 3; ++i) { p.ks[i] = a->k_stride[i]; p.vs[i] = a->v_stride[i]; }
+  p.k_codes = a->k_codes; p.k_scales = a->k_scales; p.v_codes = a->v_codes; p.v_scales = a->v_scales;
+  p.v_tail = a->v_tail; p.kv_lens = a->kv_lens;
+  p.batch = a->batch; p.kv_heads = a->kv_heads; p.n_new = a->n_new; p.kv_len = a->kv_len; p.cap = a->cap;
+  p.head_dim = a->head_dim; p.R = a->v_tile_rows;
+  p.n_vtiles_cap = (a->cap + a->v_tile_rows - 1) / a->v_tile_rows;
+  return from_hip(launch_append(p, stream));
+}
+
 qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream) {
   qk4v8_status st = validate_decode(a);
   if (st != QK4V8_OK) return st;

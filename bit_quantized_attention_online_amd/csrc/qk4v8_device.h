@@ -140,6 +140,21 @@ __device__ __forceinline__ float mask_score(float s, int slack) {
 constexpr float kLazyRescale = 8.0f;   // log2 headroom before the accumulator is rescaled
 constexpr uint32_t kFp8Ones = 0x38383838u;   // four E4M3 1.0 bytes
 
+// Maximum over the two lanes l and l^32 (v_permlane32_swap exchanges the
+// halves of the wave without an LDS round trip; max is symmetric, so the pair
+// of results gives the partner's value whichever way round they come).
+__device__ __forceinline__ float max_with_lane_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Maximum over the two lanes l and l^16 (v_permlane16_swap exchanges the
+// odd and even 16-lane rows; as above, the pair holds the partner's value).
+__device__ __forceinline__ float max_with_lane_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Online-softmax step for one 16-query block and one 128-key tile, followed
 // by the two-term FP8 split of the probabilities ("MpFA免训练量化：QK4V8混合精度
 // 在Blackwell上的推理加速实践" §2.3: scores, normalizer and V accumulation in one
@@ -156,15 +171,18 @@ constexpr uint32_t kFp8Ones = 0x38383838u;   // four E4M3 1.0 bytes
 template <int ND>
 __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run, v4f (&O)[ND], v4f& L, v8i& Phi,
                                              v8i& Plo, int& psc) {
-  // row maximum over the lane's 32 scores (three-input maxima), then across
-  // the 4 lanes that hold the same query
-  float mx = S[0][0];
+  // row maximum over the lane's 32 scores (independent chains, then a tree),
+  // then across the 4 lanes that hold the same query (l ^ 16, l ^ 32), by lane
+  // swaps rather than LDS permutes
+  float m4[4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int g = 0; g < 4; ++g) m4[g] = fmaxf(fmaxf(S[2 * g][0], S[2 * g][1]), fmaxf(S[2 * g][2], S[2 * g][3]));
 #pragma unroll
-    for (int i = (t == 0 ? 1 : 0); i < 4; ++i) mx = fmaxf(mx, S[t][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  for (int g = 0; g < 4; ++g) m4[g] = fmaxf(m4[g], fmaxf(fmaxf(S[2 * g + 1][0], S[2 * g + 1][1]),
+                                                       fmaxf(S[2 * g + 1][2], S[2 * g + 1][3])));
+  float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+  mx = max_with_lane_xor16(mx);
+  mx = max_with_lane_xor32(mx);
   const float tmax = mx * c;
   const float m_new = fmaxf(m_run, tmax);
   // wave-uniform, rarely taken: move the running max only when it grew by more
@@ -181,29 +199,32 @@ __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run,
   const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
   psc = X + 127;
   const float sh = exp2i(X), sl = exp2i(X - 4);
+  // independent passes over the 32 scores, in place: weights, hi codes (the
+  // previous tile's codes are dead here and are overwritten), residuals, lo
+  // codes
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[t][i] = __builtin_amdgcn_exp2f(fmaf(S[t][i], c, -m_use));
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(S[t][i], c, -m_use));
-    // the previous tile's codes are dead here: overwrite them in place
-    uint32_t h = e4m3_put2<false>((uint32_t)Phi[t], p[0], p[1], sh);
-    h = e4m3_put2<true>(h, p[2], p[3], sh);
-    const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, false);
-    const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, true);
-    uint32_t l = e4m3_put2<false>((uint32_t)Plo[t], p[0] - b01[0], p[1] - b01[1], sl);
-    l = e4m3_put2<true>(l, p[2] - b23[0], p[3] - b23[1], sl);
-    Phi[t] = (int)h;
-    Plo[t] = (int)l;
+    const uint32_t h = e4m3_put2<false>((uint32_t)Phi[t], S[t][0], S[t][1], sh);
+    Phi[t] = (int)e4m3_put2<true>(h, S[t][2], S[t][3], sh);
   }
-}
-
-// Maximum over the two lanes l and l^32 (v_permlane32_swap exchanges the
-// halves of the wave without an LDS round trip; max is symmetric, so the pair
-// of results gives the partner's value whichever way round they come).
-__device__ __forceinline__ float max_with_lane_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)Phi[t], sh, false);
+    const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)Phi[t], sh, true);
+    S[t][0] -= b01[0];
+    S[t][1] -= b01[1];
+    S[t][2] -= b23[0];
+    S[t][3] -= b23[1];
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t l = e4m3_put2<false>((uint32_t)Plo[t], S[t][0], S[t][1], sl);
+    Plo[t] = (int)e4m3_put2<true>(l, S[t][2], S[t][3], sl);
+  }
 }
 
 // The same step for the 32x32x64 layout: S holds the 4 key-block results of
@@ -286,6 +307,26 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+// Block-wide max over 256 threads (4 waves).
+__device__ __forceinline__ float block_max256(float v, float* red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) red[wv] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return v;
+}
+
+// Quantize 8 bf16 (one uint4) with the tile's inverse scale -> 8 E4M3 bytes.
+__device__ __forceinline__ uint2 e4m3_quantize8(uint4 w, float inv) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    b[i] = e4m3_pack2(clamp448(bf16_lo(ws[i]) * inv), clamp448(bf16_hi(ws[i]) * inv), 1.0f);
+  return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

@@ -57,4 +57,21 @@ int decode_num_splits(int batch, int kv_heads, int kv_len, int requested);
 size_t decode_workspace_bytes(int batch, int q_len, int q_heads, int kv_heads, int head_dim, int splits);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// KV-cache append: new K rows to MXFP4 and V rows to per-tile FP8 in the
+// decode cache layout (see append.hip).
+struct AppendParams {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t ks[3], vs[3];      // {batch, token, head} element strides
+  uint8_t* k_codes;
+  uint8_t* k_scales;
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  uint16_t* v_tail;          // [batch * kv_heads, R, head_dim]
+  const int32_t* kv_lens;
+  int batch, kv_heads, n_new, kv_len, cap, head_dim, R;
+  int64_t n_vtiles_cap;      // ceil(cap / R)
+};
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+
 }  // namespace qk4v8

@@ -42,26 +42,6 @@ __global__ void __launch_bounds__(256) quantize_qk_kernel(const uint16_t* __rest
   }
 }
 
-// Block-wide max over 256 threads (4 waves).
-__device__ __forceinline__ float block_max256(float v, float* red) {
-  v = wave_max(v);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  if (lane == 0) red[wv] = v;
-  __syncthreads();
-  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  return v;
-}
-
-// Quantize 8 bf16 (one uint4) with the tile's inverse scale -> 8 E4M3 bytes.
-__device__ __forceinline__ uint2 e4m3_quantize8(uint4 w, float inv) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  uint32_t b[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    b[i] = e4m3_pack2(clamp448(bf16_lo(ws[i]) * inv), clamp448(bf16_hi(ws[i]) * inv), 1.0f);
-  return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-}
-
 // One workgroup (256 threads) per (group, tile of R rows).  The tile stays in
 // registers (VPT uint4 per thread) between the absmax and the encode phase.
 template <int VPT>

@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "QK4V8_OK", 1: "QK4V8_ERR_NULL", 2: "QK4V8_ERR_SHAPE", 3: "QK
 
 EXPORTED = ["qk4v8_abi_version", "qk4v8_status_string", "qk4v8_quantize_qk", "qk4v8_quantize_v",
             "qk4v8_prefill_workspace_bytes", "qk4v8_attn_prefill", "qk4v8_prefill_pack_kv",
-            "qk4v8_attn_prefill_packed", "qk4v8_decode_workspace_bytes", "qk4v8_attn_decode"]
+            "qk4v8_attn_prefill_packed", "qk4v8_decode_workspace_bytes", "qk4v8_attn_decode",
+            "qk4v8_kv_append"]
 
 
 class PrefillArgs(ctypes.Structure):
@@ -45,6 +46,16 @@ class DecodeArgs(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("v_tile_rows", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class AppendArgs(ctypes.Structure):
+    _fields_ = [("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+                ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
+                ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p), ("v_tail", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("n_new", ctypes.c_int32),
+                ("kv_len", ctypes.c_int32), ("cap", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("v_tile_rows", ctypes.c_int32)]
 
 
 class QK4V8Error(RuntimeError):
@@ -80,6 +91,8 @@ def lib():
         L.qk4v8_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
         L.qk4v8_attn_decode.restype = ctypes.c_int
         L.qk4v8_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+        L.qk4v8_kv_append.restype = ctypes.c_int
+        L.qk4v8_kv_append.argtypes = [ctypes.POINTER(AppendArgs), ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -248,3 +261,41 @@ def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256
     a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _check(lib().qk4v8_attn_decode(ctypes.byref(a), _stream(stream)), "qk4v8_attn_decode")
     return (o, lse) if return_lse else o
+
+
+def kv_append(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows=256,
+              kv_lens=None, stream=None):
+    """Quantize n_new tokens per sequence into a decode cache (in place).
+    k_new, v_new [B, n_new, Hkv, d] bf16 (token-major, strided); cache tensors as
+    for attn_decode with capacity cap = k_codes.shape[2]; v_tail [B, Hkv, R, d]
+    bf16 keeps the source rows of each sequence's partial V tile.  kv_lens
+    (device int32 [B]) or kv_len: tokens already cached; not modified."""
+    _bits16(k_new)
+    _bits16(v_new)
+    if kv_lens is not None and kv_lens.dtype != torch.int32:
+        raise TypeError("kv_lens must be int32")
+    B, n_new, Hkv, d = k_new.shape
+    if B == 0 or n_new == 0:
+        return
+    for t in (k_new, v_new):
+        if t.stride(-1) != 1:
+            raise ValueError("innermost stride must be 1")
+    if tuple(v_new.shape) != (B, n_new, Hkv, d):
+        raise ValueError("k_new and v_new shapes differ")
+    for t in (k_codes, k_scales, v_codes, v_scales, v_tail):
+        if not t.is_contiguous():
+            raise ValueError("cache tensors and v_tail must be contiguous")
+    if tuple(v_tail.shape) != (B, Hkv, v_tile_rows, d):
+        raise ValueError("v_tail must be [B, Hkv, v_tile_rows, d]")
+    a = AppendArgs()
+    a.k_new, a.v_new = k_new.data_ptr(), v_new.data_ptr()
+    for i, ax in enumerate((0, 1, 2)):
+        a.k_stride[i] = k_new.stride(ax)
+        a.v_stride[i] = v_new.stride(ax)
+    a.k_codes, a.k_scales, a.v_codes, a.v_scales = (k_codes.data_ptr(), k_scales.data_ptr(), v_codes.data_ptr(),
+                                                    v_scales.data_ptr())
+    a.v_tail = v_tail.data_ptr()
+    a.kv_lens = kv_lens.data_ptr() if kv_lens is not None else None
+    a.batch, a.kv_heads, a.n_new, a.kv_len = B, Hkv, n_new, int(kv_len)
+    a.cap, a.head_dim, a.v_tile_rows = k_codes.shape[2], d, v_tile_rows
+    _check(lib().qk4v8_kv_append(ctypes.byref(a), _stream(stream)), "qk4v8_kv_append")

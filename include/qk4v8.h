@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QK4V8_ABI_VERSION 1
+#define QK4V8_ABI_VERSION 2
 
 typedef enum {
   QK4V8_OK = 0,
@@ -207,6 +207,50 @@ typedef struct {
 /* Workspace bytes qk4v8_attn_decode needs for these sizes (0 on bad sizes). */
 size_t qk4v8_decode_workspace_bytes(const qk4v8_decode_args* a);
 qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream);
+
+/*
+ * KV-cache append (MpFA page §6.1: the cache is kept quantized, so new tokens
+ * are quantized as they are written; §5.2).  Writes n_new new tokens per
+ * sequence into the cache layout that qk4v8_attn_decode reads: K rows to MXFP4
+ * (each row independently) and V rows to E4M3FN in the per-(batch, kv-head)
+ * tiles of v_tile_rows rows.  A V tile that is still filling carries the scale
+ * of all the rows it holds so far, so after any sequence of appends the cache
+ * holds exactly what qk4v8_quantize_qk / qk4v8_quantize_v give for the whole
+ * sequence.  When new rows raise a tile's E8M0 exponent, its earlier rows are
+ * re-quantized from their bf16 values, which `v_tail` keeps for the last,
+ * partial tile of every sequence.
+ *
+ *   k_new, v_new : bf16 [batch, n_new, kv_heads, head_dim], strides
+ *                  k_stride / v_stride = {batch, token, head} (multiples of 8).
+ *   kv_lens      : device int32 [batch]: tokens in each sequence's cache before
+ *                  this call (NULL: kv_len for every sequence).  Not modified;
+ *                  the caller advances it.  A sequence whose length is negative
+ *                  or whose length + n_new exceeds cap is left untouched.
+ *   k_codes, k_scales, v_codes, v_scales : the cache (qk4v8_attn_decode layout,
+ *                  capacity cap tokens), updated in place.
+ *   v_tail       : bf16 [batch, kv_heads, v_tile_rows, head_dim], contiguous,
+ *                  owned by the caller and updated by the call.  Before the
+ *                  call, row i of (b, h) must hold the source V row
+ *                  R * floor(len_b / R) + i for i < len_b % R (as the previous
+ *                  append left it; nothing is needed when len_b % R == 0).
+ *   head_dim ∈ {64, 128}; v_tile_rows ∈ {32, 64, 128, 256}; n_new >= 0 (0 is a
+ *   no-op); with kv_lens NULL, 0 <= kv_len and kv_len + n_new <= cap.
+ */
+typedef struct {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  uint8_t* k_codes;
+  uint8_t* k_scales;
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  uint16_t* v_tail;
+  const int32_t* kv_lens;
+  int32_t batch, kv_heads, n_new, kv_len, cap, head_dim, v_tile_rows;
+} qk4v8_append_args;
+
+qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.qk4v8_abi_version() == 1
+    assert L.qk4v8_abi_version() == 2
     for s in range(7):
         assert L.qk4v8_status_string(s)
 
@@ -116,3 +116,38 @@ def test_decode_workspace_query():
     rows = 2 * 8 * 4 * 8
     assert L.qk4v8_decode_workspace_bytes(ctypes.byref(a)) >= rows * (128 * 4 + 4)
     assert L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(q_len=9))) == 0
+
+
+def _append(**kw):
+    a = ops.AppendArgs()
+    a.k_new = a.v_new = a.k_codes = a.k_scales = a.v_codes = a.v_scales = a.v_tail = 4096
+    a.k_stride[:] = [8 * 128, 8 * 128, 128]
+    a.v_stride[:] = [8 * 128, 8 * 128, 128]
+    a.batch, a.kv_heads, a.n_new, a.kv_len, a.cap = 2, 8, 1, 1000, 1024
+    a.head_dim, a.v_tile_rows = 128, 256
+    for k, v in kw.items():
+        if k.endswith("stride"):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 2),
+    (dict(v_tile_rows=100), 2),
+    (dict(n_new=-1), 2),
+    (dict(kv_heads=0), 2),
+    (dict(kv_len=1020, n_new=8), 2),           # does not fit the capacity
+    (dict(kv_len=-1), 2),
+    (dict(k_stride=[8 * 128, 8 * 128, 100]), 3),
+    (dict(v_stride=[8 * 128, -8, 128]), 3),
+    (dict(v_tail=0), 1),
+    (dict(k_new=0), 1),
+    (dict(v_codes=4100), 3),                   # not 8-byte aligned
+    (dict(k_codes=4104), 3),                   # not 16-byte aligned
+    (dict(n_new=0), 0),                        # no-op
+    (dict(batch=0), 0),
+])
+def test_append_validation(kw, status):
+    assert ops.lib().qk4v8_kv_append(ctypes.byref(_append(**kw)), None) == status
