@@ -12,11 +12,12 @@
 // re-quantization would give); when it grows, the tile is re-quantized from
 // the bf16 rows the caller's tail buffer keeps for the partial tile.
 //
-// Three launches on the caller's stream:
-//   append_k_kernel     thread per (b, token, kv-head, 32-element block)
-//   append_v_kernel     workgroup per (b, kv-head, tile touched by the append)
-//   append_tail_kernel  copies the new rows of each new partial tile into the
-//                       tail buffer (after append_v_kernel has read it)
+// One launch: workgroups [0, bh * slots) handle the V tiles touched by the
+// append, one per (b, kv-head, tile); the rest quantize the new K rows, one
+// thread per (b, token, kv-head, 32-element block).  Only the workgroup of the
+// first touched tile of a sequence reads that sequence's tail buffer, and the
+// same workgroup writes the new tail rows after a barrier, so no other
+// workgroup races with it.
 #include "qk4v8_device.h"
 #include "qk4v8_launch.h"
 
@@ -31,9 +32,8 @@ __device__ __forceinline__ int append_len(const AppendParams& p, int b) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(256) append_k_kernel(AppendParams p, int64_t total) {
+__device__ __forceinline__ void append_k(const AppendParams& p, int64_t id, int64_t total) {
   constexpr int NB = D / 32;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (id >= total) return;
   const int g = (int)(id % NB);
   const int64_t rest = id / NB;
@@ -61,11 +61,10 @@ __global__ void __launch_bounds__(256) append_k_kernel(AppendParams p, int64_t t
 // the tile in [len, end) are new (from v_new); rows in [tile*R, len) were
 // cached earlier and their bf16 values are in the tail buffer.
 template <int D>
-__global__ void __launch_bounds__(256) append_v_kernel(AppendParams p, int slots) {
+__device__ __forceinline__ void append_v(const AppendParams& p, int64_t wg, int slots, float* red) {
   constexpr int CPR = D / 8;                        // 16-byte chunks per row
-  __shared__ float red[4];
-  const int slot = (int)(blockIdx.x % slots);
-  const int64_t bh = blockIdx.x / slots;
+  const int slot = (int)(wg % slots);
+  const int64_t bh = wg / slots;
   const int b = (int)(bh / p.kv_heads), h = (int)(bh - (int64_t)b * p.kv_heads);
   const int len = append_len(p, b);
   if (len < 0) return;
@@ -113,27 +112,29 @@ __global__ void __launch_bounds__(256) append_v_kernel(AppendParams p, int slots
     *reinterpret_cast<uint2*>(codes + (int64_t)r * D + cc * 8) = e4m3_quantize8(w, inv);
   }
   if (threadIdx.x == 0) *scale_ptr = (uint8_t)(X + 127);
+  if (slot != 0) return;
+  // the new rows of the sequence's last, partial tile go to the tail buffer,
+  // after every read of it above (rows already there stay)
+  __syncthreads();
+  const int t_last = end / R;
+  const int first = max(t_last * R, len);
+  const int nvec_tail = (end - first) * CPR;
+  uint16_t* const tail = p.v_tail + bh * R * D;
+  for (int vi = threadIdx.x; vi < nvec_tail; vi += 256) {
+    const int r = first + vi / CPR, cc = vi % CPR;
+    const uint4 w = *reinterpret_cast<const uint4*>(p.v_new + b * p.vs[0] + (int64_t)(r - len) * p.vs[1] +
+                                                    h * p.vs[2] + cc * 8);
+    *reinterpret_cast<uint4*>(tail + (int64_t)(r - t_last * R) * D + cc * 8) = w;
+  }
 }
 
-// Thread per (b, h, tail row, 16-byte chunk): rows of the new last partial tile
-// that arrived in this call are copied into the tail buffer.
 template <int D>
-__global__ void __launch_bounds__(256) append_tail_kernel(AppendParams p, int64_t total) {
-  constexpr int CPR = D / 8;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= total) return;
-  const int cc = (int)(id % CPR);
-  const int i = (int)((id / CPR) % p.R);
-  const int64_t bh = id / ((int64_t)CPR * p.R);
-  const int b = (int)(bh / p.kv_heads), h = (int)(bh - (int64_t)b * p.kv_heads);
-  const int len = append_len(p, b);
-  if (len < 0) return;
-  const int end = len + p.n_new;
-  const int r = (end / p.R) * p.R + i;              // row i of the last tile
-  if (r >= end || r < len) return;                  // absent, or already in the tail
-  const uint4 w = *reinterpret_cast<const uint4*>(p.v_new + b * p.vs[0] + (int64_t)(r - len) * p.vs[1] +
-                                                  h * p.vs[2] + cc * 8);
-  *reinterpret_cast<uint4*>(p.v_tail + (bh * p.R + i) * D + cc * 8) = w;
+__global__ void __launch_bounds__(256) append_kernel(AppendParams p, int slots, int64_t v_wgs, int64_t total_k) {
+  __shared__ float red[4];
+  if ((int64_t)blockIdx.x < v_wgs)
+    append_v<D>(p, blockIdx.x, slots, red);
+  else
+    append_k<D>(p, ((int64_t)blockIdx.x - v_wgs) * 256 + threadIdx.x, total_k);
 }
 
 }  // namespace
@@ -141,18 +142,13 @@ __global__ void __launch_bounds__(256) append_tail_kernel(AppendParams p, int64_
 template <int D>
 static hipError_t launch_append_d(const AppendParams& p, hipStream_t stream) {
   const int64_t bh = (int64_t)p.batch * p.kv_heads;
-  const int64_t total_k = bh * p.n_new * (D / 32);
-  hipLaunchKernelGGL((append_k_kernel<D>), dim3((unsigned)((total_k + 255) / 256)), dim3(256), 0, stream, p, total_k);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // tiles touched per sequence: at most ceil(n_new / R) + 1
   const int slots = (p.n_new + p.R - 1) / p.R + 1;
-  hipLaunchKernelGGL((append_v_kernel<D>), dim3((unsigned)(bh * slots)), dim3(256), 0, stream, p, slots);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t total_t = bh * p.R * (D / 8);
-  hipLaunchKernelGGL((append_tail_kernel<D>), dim3((unsigned)((total_t + 255) / 256)), dim3(256), 0, stream, p,
-                     total_t);
+  const int64_t v_wgs = bh * slots;
+  const int64_t total_k = bh * p.n_new * (D / 32);
+  const int64_t k_wgs = (total_k + 255) / 256;
+  hipLaunchKernelGGL((append_kernel<D>), dim3((unsigned)(v_wgs + k_wgs)), dim3(256), 0, stream, p, slots, v_wgs,
+                     total_k);
   return hipGetLastError();
 }
 

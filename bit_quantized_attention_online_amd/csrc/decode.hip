@@ -148,12 +148,17 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
       constexpr int i = decltype(I)::value;
       const int ci = tid + i * NT;
       if (VCH % NT == 0 || ci < VCH) {
-        const int j = j0_ + ci / NC;
-        const int key = min(j, a.cap - 1);
+        const int key = min(j0_ + ci / NC, a.cap - 1);
         rv[i] = *reinterpret_cast<const v4i*>(gv + (int64_t)key * D + (ci % NC) * 16);
-        if (j >= kvlen) rv[i] = v4i{0, 0, 0, 0};
       }
     });
+    if (j0_ + 128 > kvlen) {    // only the tile that crosses the end of the sequence
+      static_for<VPT>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const int ci = tid + i * NT;
+        if ((VCH % NT == 0 || ci < VCH) && j0_ + ci / NC >= kvlen) rv[i] = v4i{0, 0, 0, 0};
+      });
+    }
     static_for<SPT>([&](auto I) {
       constexpr int i = decltype(I)::value;
       const int ki = tid + i * NT;
