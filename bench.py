@@ -106,7 +106,24 @@ def bench_prefill(torch, ops, synth, steps, warmup):
     assert torch.isfinite(pp.o.float()).all().item(), "non-finite prefill output"
     pairs = w["B"] * w["Hq"] * causal_pairs(w["Nq"], w["Nk"])
     flops = pairs * 4.0 * w["d"]
-    return dict(w=w, wall_ms=wall * 1e3 / steps, pack_ms=pack_ms, attn_ms=attn_ms, flops=flops, pairs=pairs)
+    # fast mode (single-term FP8 probabilities) on the same inputs
+    ppf = ops.PackedPrefill(qd, kd, vd, causal=True, softmax_scale=1.0 / math.sqrt(w["d"]),
+                            v_tile_rows=w["v_tile_rows"], p_terms=1)
+    ppf.pack()
+    settle(torch, ppf.attend, seconds=0.2)
+    for _ in range(warmup):
+        ppf.attend()
+    evf = [Events(torch, 2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evf:
+        e.record(0, stream)
+        ppf.attend(stream)
+        e.record(1, stream)
+    torch.cuda.synchronize()
+    fast_ms = sum(e.ms(0, 1) for e in evf) / steps
+    assert torch.isfinite(ppf.o.float()).all().item(), "non-finite fast-mode output"
+    return dict(w=w, wall_ms=wall * 1e3 / steps, pack_ms=pack_ms, attn_ms=attn_ms, flops=flops, pairs=pairs,
+                fast_ms=fast_ms)
 
 
 def build_cache(torch, ops, w, seed):
@@ -303,6 +320,12 @@ def main():
                    "algorithmic_flops": pf["flops"]},
         "wall_ms_per_step": round(pf["wall_ms"], 4),
         "prefill_breakdown_ms": {"pack_kv": round(pf["pack_ms"], 4), "attention": round(pf["attn_ms"], 4)},
+        "prefill_fast_mode": {"p_terms": 1, "attention_ms": round(pf["fast_ms"], 4),
+                              "value": round(pf["flops"] / (pf["fast_ms"] * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                              "frac_of_mixed_peak": round(pf["flops"] / (pf["fast_ms"] * 1e-3) / 1e12
+                                                          / PEAK_MIXED_TFLOPS, 4),
+                              "note": "single-term E4M3 probabilities; about 2e-2 relative L2 from exact attention, "
+                                      "outside the 5e-3 gate of the default path"},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel<128,causal>",
                      "achieved": round(attn_tflops, 1), "peak": round(PEAK_MIXED_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_MIXED_TFLOPS, 4), "traffic": traffic},

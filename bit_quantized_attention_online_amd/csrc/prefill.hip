@@ -294,7 +294,8 @@ struct AttnArgs {
 // its chunks of tile k+2 may still be in flight), which publishes tile k+1
 // before its first QK^T in phase 2k+2.  A tile thus has about three phases to
 // arrive.
-template <int D, bool CAUSAL>
+// FAST: single-term E4M3 probabilities (integral running maximum, no lo term).
+template <int D, bool CAUSAL, bool FAST>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_kernel(AttnArgs a) {
   using TB = TileBytes<D>;
   constexpr int NS = TB::NS;        // QK^T contraction steps (64 head_dim each)
@@ -449,14 +450,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (j < NDB) {
           O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][0], Phi[0], O[j], vsc0, psc);
-          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][0], Plo[0], O[j], vsc0, psc - 4);
+          if constexpr (!FAST) O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][0], Plo[0], O[j], vsc0, psc - 4);
           O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][1], Phi[1], O[j], vsc1, psc);
-          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][1], Plo[1], O[j], vsc1, psc - 4);
+          if constexpr (!FAST) O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][1], Plo[1], O[j], vsc1, psc - 4);
         } else {
           L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[0], L, 127, psc);
-          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[0], L, 127, psc - 4);
+          if constexpr (!FAST) L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[0], L, 127, psc - 4);
           L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[1], L, 127, psc);
-          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[1], L, 127, psc - 4);
+          if constexpr (!FAST) L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[1], L, 127, psc - 4);
         }
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -484,7 +485,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[kb][i] = mask_score(S[kb][i], lim - (32 * kb + i));
     }
-    softmax_tile32<NDB>(S, cexp, m_run, O, L, Phi, Plo, psc);
+    if constexpr (FAST)
+      softmax_tile32_single<NDB>(S, cexp, m_run, O, L, Phi, psc);
+    else
+      softmax_tile32<NDB>(S, cexp, m_run, O, L, Phi, Plo, psc);
   };
 
   // one iteration of the schedule for tile k; the first (no P·V yet) and the
@@ -513,7 +517,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       valu_step(k);
       static_for<2>([&](auto I) {
         keep_in_vgprs(Phi[decltype(I)::value]);
-        keep_in_vgprs(Plo[decltype(I)::value]);
+        if constexpr (!FAST) keep_in_vgprs(Plo[decltype(I)::value]);
       });
     }
     if (grp == 0 && k + 1 < nt) wait_dma(pending);
@@ -590,10 +594,14 @@ static hipError_t launch_attn_d(const PrefillParams& p, hipStream_t stream) {
   a.xblocks = p.batch * p.kv_heads * (a.group / a.heads_per_wg);
   a.pos_groups = (p.seq_q + rows_per_wg - 1) / rows_per_wg;
   const dim3 grid((unsigned)((int64_t)a.xblocks * a.pos_groups));
-  if (p.causal)
-    hipLaunchKernelGGL((attn_kernel<D, true>), grid, dim3(kWaves * 64), 0, stream, a);
+  if (p.causal && p.single_term)
+    hipLaunchKernelGGL((attn_kernel<D, true, true>), grid, dim3(kWaves * 64), 0, stream, a);
+  else if (p.causal)
+    hipLaunchKernelGGL((attn_kernel<D, true, false>), grid, dim3(kWaves * 64), 0, stream, a);
+  else if (p.single_term)
+    hipLaunchKernelGGL((attn_kernel<D, false, true>), grid, dim3(kWaves * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, false>), grid, dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<D, false, false>), grid, dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ qk4v8_status validate_prefill(const qk4v8_prefill_args* a) {
   if (a->causal && a->seq_q > a->seq_k) return QK4V8_ERR_SHAPE;
   if (!good_scale(a->softmax_scale)) return QK4V8_ERR_SHAPE;
   if (a->seq_q > (1 << 30) || a->seq_k > (1 << 30)) return QK4V8_ERR_SHAPE;
+  if (a->p_terms != 0 && a->p_terms != 1 && a->p_terms != 2) return QK4V8_ERR_SHAPE;
   return QK4V8_OK;
 }
 
@@ -181,6 +182,7 @@ qk4v8_status run_prefill(const qk4v8_prefill_args* a, hipStream_t stream, int pa
   }
   p.batch = a->batch; p.q_heads = a->q_heads; p.kv_heads = a->kv_heads; p.seq_q = a->seq_q; p.seq_k = a->seq_k;
   p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows; p.causal = a->causal;
+  p.single_term = a->p_terms == 1;
   p.softmax_scale = a->softmax_scale;
   p.ws = static_cast<uint8_t*>(a->workspace);
   if (parts & kPack) {

@@ -303,6 +303,55 @@ __device__ __forceinline__ void softmax_tile32(v16f (&S)[4], float c, float& m_r
     }
 }
 
+// Single-term variant of softmax_tile32 (fast mode): P is one E4M3 term per
+// weight.  The running maximum is kept integral, so every rescale is an exact
+// power of two and the E4M3 rounding of p / 2^X = 2^(s*c - floor(tmax) + 7)
+// depends only on the scores and on the tile's maximum, not on when the
+// maximum moved: the result is the same for any order of the tiles.
+template <int NO>
+__device__ __forceinline__ void softmax_tile32_single(v16f (&S)[4], float c, float& m_run, v16f (&O)[NO], v16f& L,
+                                                      v8i (&Phi)[2], int& psc) {
+  float m4[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    float a = fmaxf(S[kb][0], S[kb][1]), b = fmaxf(S[kb][2], S[kb][3]);
+#pragma unroll
+    for (int i = 4; i < 16; i += 4) {
+      a = fmaxf(a, fmaxf(S[kb][i], S[kb][i + 1]));
+      b = fmaxf(b, fmaxf(S[kb][i + 2], S[kb][i + 3]));
+    }
+    m4[kb] = fmaxf(a, b);
+  }
+  const float mx = max_with_lane_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+  const float tmax = mx * c;
+  const float m_new = ceilf(fmaxf(m_run, tmax));           // integral (or -inf)
+  const bool grow = __builtin_amdgcn_readfirstlane((int)__any(m_new > m_run + kLazyRescale)) != 0;
+  if (__builtin_expect(grow, 0)) {
+    // 2^(m_run - m_new) built from its exponent bits: exact
+    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2i((int)fmaxf(m_run - m_new, -126.0f));
+#pragma unroll
+    for (int o = 0; o < NO; ++o) O[o] *= alpha;
+    L *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+  const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
+  psc = X + 127;
+  const float sh = exp2i(X);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[kb][i] = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -m_use));
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int dw = 4 * (kb & 1) + w;
+      uint32_t h = e4m3_put2<false>((uint32_t)Phi[kb >> 1][dw], S[kb][4 * w], S[kb][4 * w + 1], sh);
+      Phi[kb >> 1][dw] = (int)e4m3_put2<true>(h, S[kb][4 * w + 2], S[kb][4 * w + 3], sh);
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -33,6 +33,7 @@ struct PrefillParams {
   float* lse;
   int64_t qs[3], ks[3], vs[3], os[3];
   int batch, q_heads, kv_heads, seq_q, seq_k, head_dim, v_tile_rows, causal;
+  int single_term;           // 1: fast mode (one E4M3 term per probability)
   float softmax_scale;
   uint8_t* ws;
 };

@@ -33,7 +33,8 @@ class PrefillArgs(ctypes.Structure):
                 ("seq_q", ctypes.c_int32), ("seq_k", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("v_tile_rows", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("p_terms", ctypes.c_int32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -149,7 +150,7 @@ def quantize_v(v, tile_rows, stream=None):
     return codes, scales
 
 
-def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows):
+def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms=2):
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
     a = PrefillArgs()
@@ -162,6 +163,7 @@ def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows):
     a.batch, a.q_heads, a.kv_heads, a.seq_q, a.seq_k, a.head_dim = B, Hq, Hkv, Nq, Nk, d
     a.v_tile_rows, a.causal = v_tile_rows, int(bool(causal))
     a.softmax_scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
+    a.p_terms = p_terms
     return a
 
 
@@ -172,15 +174,15 @@ def prefill_workspace_bytes(q, k, v, causal=False, softmax_scale=None, v_tile_ro
 
 
 def attn_prefill(q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, out=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, p_terms=2):
     """QK4V8 prefill.  q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d] bf16 (any strides
     with unit innermost).  Returns o [B, Hq, Nq, d] bf16 (and lse fp32
-    [B, Hq, Nq] when return_lse)."""
+    [B, Hq, Nq] when return_lse).  p_terms=1 selects the single-term fast mode."""
     for t in (q, k, v):
         _bits16(t)
     o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-    a = _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows)
+    a = _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms)
     need = lib().qk4v8_prefill_workspace_bytes(ctypes.byref(a))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -194,12 +196,12 @@ class PackedPrefill:
     ``pack()`` quantizes K/V into the workspace, ``attend()`` runs the
     attention kernel from it (used to time the two halves separately)."""
 
-    def __init__(self, q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False):
+    def __init__(self, q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, p_terms=2):
         for t in (q, k, v):
             _bits16(t)
         self.o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
         self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-        self.args = _prefill_args(q, k, v, self.o, self.lse, causal, softmax_scale, v_tile_rows)
+        self.args = _prefill_args(q, k, v, self.o, self.lse, causal, softmax_scale, v_tile_rows, p_terms)
         need = lib().qk4v8_prefill_workspace_bytes(ctypes.byref(self.args))
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self.args.workspace, self.args.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()

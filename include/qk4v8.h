@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QK4V8_ABI_VERSION 2
+#define QK4V8_ABI_VERSION 3
 
 typedef enum {
   QK4V8_OK = 0,
@@ -127,6 +127,20 @@ qk4v8_status qk4v8_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int3
  *   workspace : device scratch of at least qk4v8_prefill_workspace_bytes()
  *               bytes, 256-byte aligned; it receives the call's quantized
  *               copies of K and V.  Contents on return are unspecified.
+ *   p_terms   : how the probabilities enter the FP8 P·V product.
+ *               0 or 2 (default): two E4M3 terms per weight, hi = E4M3(p/2^X)
+ *               and lo = E4M3((p - hi*2^X) / 2^(X-4)), with one E8M0 range
+ *               exponent X per query row and 128-key tile; the result meets
+ *               the accuracy of exact attention on the quantized operands to
+ *               about 2e-3 relative L2.
+ *               1 (fast mode): one E4M3 term per weight, an integral running
+ *               maximum (every rescale an exact power of two) and the same
+ *               range exponent; half the P·V matrix work and fewer vector
+ *               instructions, at about 2e-2 relative L2 from exact attention.
+ *               Its result is independent of the tiling: with base-2 scores
+ *               t = s*log2(e) and 128-key blocks B aligned at multiples of 128,
+ *               p~_j = 2^X_B * E4M3(2^(t_j - X_B)), X_B = floor(max_B t) - 7, and
+ *               o = sum_j p~_j v_j / sum_j p~_j.
  */
 typedef struct {
   const uint16_t* q;
@@ -142,6 +156,7 @@ typedef struct {
   float softmax_scale;
   void* workspace;
   size_t workspace_bytes;
+  int32_t p_terms;
 } qk4v8_prefill_args;
 
 /* Workspace bytes qk4v8_attn_prefill needs for these sizes (0 on bad sizes). */

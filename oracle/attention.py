@@ -22,6 +22,7 @@ bottom-right mask.
 
 import numpy as np
 
+from .formats import e4m3_decode, e4m3_encode
 from .quant import dequantize_qk, dequantize_v, quantize_qk, quantize_v
 
 _CHUNK_ELEMS = 1 << 25
@@ -133,3 +134,81 @@ def qk4v8_decode(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens, v_tile_r
         o[b] = ob[0].transpose(1, 0, 2)
         lse[b] = lb[0].T
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Single-term FP8 probabilities (the library's fast mode).
+#
+# P·V on FP8 (E4M3) with one term per probability.  Its definition does not
+# depend on how keys are tiled: with base-2 scores t_ij = s_ij * log2(e), the
+# keys of a row are grouped in blocks of 128 (key indices [128a, 128a + 128)),
+# each block gets the range exponent X = floor(max_j t_ij) - 7 over its visible
+# keys, and each weight is rounded to E4M3 on that range:
+#     p~_ij = 2^X * E4M3_RNE(2^(t_ij - X))       (2^(t - X) < 256, no saturation)
+#     o_i   = sum_j p~_ij v_j / sum_j p~_ij,   lse_i = ln(sum_j p~_ij)
+# A common factor 2^M per row (M any integer) cancels in o and is added back
+# in lse.  The two-term FP8 split of the default path is a kernel rounding
+# detail below the gate and is not modelled here (see ``attention``).
+# ---------------------------------------------------------------------------
+
+FAST_P_BLOCK = 128
+FAST_P_HEADROOM = 7
+_LOG2E = 1.4426950408889634
+
+
+def _rows_attention_fast(q, k, v, sigma, limits):
+    s = sigma * (q @ k.T)
+    Nk = k.shape[0]
+    cols = np.arange(Nk)
+    t = np.where(cols[None, :] <= limits[:, None], s * _LOG2E, -np.inf)
+    M = np.floor(t.max(axis=1))                                  # common integer shift per row
+    t = t - M[:, None]
+    nb = -(-Nk // FAST_P_BLOCK)
+    tp = np.full((t.shape[0], nb * FAST_P_BLOCK), -np.inf)
+    tp[:, :Nk] = t
+    tb = tp.reshape(t.shape[0], nb, FAST_P_BLOCK)
+    bmax = tb.max(axis=2)
+    X = np.where(np.isfinite(bmax), np.floor(bmax) - FAST_P_HEADROOM, 0.0)
+    y = np.exp2(tb - X[:, :, None])                              # 0 for masked keys
+    p = e4m3_decode(e4m3_encode(y)) * np.exp2(X)[:, :, None]
+    p = p.reshape(t.shape[0], nb * FAST_P_BLOCK)[:, :Nk]
+    l = p.sum(axis=1)
+    o = (p @ v) / l[:, None]
+    return o, (M + np.log2(l)) * np.log(2.0)
+
+
+def attention_fast_p(q, k, v, softmax_scale, causal, rows=None):
+    """Attention with single-term E4M3 probabilities (definition above);
+    same arguments and returns as ``attention``."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, R, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    G = Hq // Hkv
+    if rows is None:
+        pos, Nq = np.arange(R), R
+    else:
+        pos, Nq = np.asarray(rows[0]), rows[1]
+    sigma = float(np.float32(softmax_scale))
+    limits = pos + (Nk - Nq) if causal else np.full(R, Nk - 1)
+    o = np.zeros((B, Hq, R, d))
+    lse = np.zeros((B, Hq, R))
+    step = max(1, _CHUNK_ELEMS // max(Nk, 1))
+    for b in range(B):
+        for h in range(Hq):
+            for r0 in range(0, R, step):
+                sl = slice(r0, min(R, r0 + step))
+                o[b, h, sl], lse[b, h, sl] = _rows_attention_fast(q[b, h, sl], k[b, h // G], v[b, h // G], sigma,
+                                                                  limits[sl])
+    return o, lse
+
+
+def qk4v8_prefill_fast(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_rows, rows=None):
+    """``qk4v8_prefill`` with single-term FP8 probabilities."""
+    qh = dequantize_qk(*quantize_qk(q_bits))
+    kh = dequantize_qk(*quantize_qk(k_bits))
+    B, Hkv, Nk, d = v_bits.shape
+    vc, vs = quantize_v(v_bits.reshape(B * Hkv, Nk, d), v_tile_rows)
+    vh = dequantize_v(vc, vs, v_tile_rows).reshape(B, Hkv, Nk, d)
+    return attention_fast_p(qh, kh, vh, softmax_scale, causal, rows=rows)

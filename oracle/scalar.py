@@ -97,3 +97,29 @@ def attention_rows(q, k, v, sigma, causal):
         out.append([math.fsum(p[j] * v[j][c] for j in range(len(p))) / l for c in range(len(v[0]))])
         lses.append(m + math.log(l))
     return out, lses
+
+
+def attention_rows_fast_p(q, k, v, sigma, causal, block=128, headroom=7):
+    """Single-term E4M3 probabilities by loops: base-2 scores t = s*log2(e),
+    keys in blocks [block*a, block*a + block), each block's range exponent
+    X = floor(max t) - headroom (floor found by stepping), each weight rounded
+    by scanning every E4M3 code.  Returns (o rows, lse list)."""
+    nq, nk = len(q), len(k)
+    log2e = 1.0 / math.log(2.0)
+    out, lses = [], []
+    for i in range(nq):
+        last = i + (nk - nq) if causal else nk - 1
+        t = [sigma * math.fsum(a * b for a, b in zip(q[i], k[j])) * log2e for j in range(last + 1)]
+        M = max(t)
+        Mi = math.floor(M)
+        p = []
+        for j in range(last + 1):
+            a = j // block
+            bmax = max(t[a * block:min((a + 1) * block, last + 1)]) - Mi
+            X = floor_log2(2.0 ** bmax) - headroom
+            y = 2.0 ** (t[j] - Mi - X)
+            p.append(e4m3_value(nearest_code(y, range(128), e4m3_value)) * 2.0 ** X)
+        l = math.fsum(p)
+        out.append([math.fsum(p[j] * v[j][c] for j in range(len(p))) / l for c in range(len(v[0]))])
+        lses.append((Mi + math.log2(l)) * math.log(2.0))
+    return out, lses

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.qk4v8_abi_version() == 2
+    assert L.qk4v8_abi_version() == 3
     for s in range(7):
         assert L.qk4v8_status_string(s)
 
@@ -67,6 +67,7 @@ def _prefill(**kw):
     (dict(causal=2), 2), (dict(seq_q=65), 2), (dict(softmax_scale=0.0), 2), (dict(softmax_scale=float("nan")), 2),
     (dict(q=None), 1), (dict(q_stride=[64 * 128, 128, 36]), 3), (dict(o_stride=[64 * 128, 128, 4]), 3),
     (dict(k=4100), 3), (dict(workspace=None), 5), (dict(workspace=1 << 20 | 8), 5), (dict(workspace_bytes=16), 5),
+    (dict(p_terms=3), 2),
 ])
 def test_prefill_validation(kw, status):
     a = _prefill(**kw)

@@ -122,3 +122,48 @@ def test_prefill_long_causal_workload_sampled_rows(gpu):
     o_rows = from_dev_bf16(o[:, :, torch.from_numpy(rows).cuda()])
     ro, _ = oatt.qk4v8_prefill(q[:, :, rows], k, v, 1 / math.sqrt(128), True, 64, rows=(rows, N))
     assert_attn_close(o_rows, ro, "workload 4 sampled rows")
+
+
+FAST_CASES = [
+    (1, 1, 1, 256, 256, 64, False, 64),
+    (2, 4, 2, 300, 300, 128, True, 64),
+    (1, 8, 1, 77, 333, 128, True, 32),
+    (1, 16, 2, 260, 260, 128, True, 64),
+    (1, 4, 4, 513, 700, 128, False, 256),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,R", FAST_CASES)
+def test_prefill_fast_mode(gpu, B, Hq, Hkv, Nq, Nk, d, causal, R):
+    """Single-term FP8 probabilities against their own (tile-independent)
+    oracle; the distance to exact attention is printed, not gated."""
+    from bit_quantized_attention_online_amd import ops
+    q, k, v = _inputs(B, Hq, Hkv, Nq, Nk, d, seed=B * 1000 + Nq + Nk + d + 7)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[case] prefill fast q{q.shape} k{k.shape} causal={causal} R={R}", flush=True)
+    o, l = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=causal, softmax_scale=scale, v_tile_rows=R,
+                            return_lse=True, p_terms=1)
+    torch.cuda.synchronize()
+    ro, rl = oatt.qk4v8_prefill_fast(q, k, v, scale, causal, R)
+    got = from_dev_bf16(o)
+    assert_attn_close(got, ro, f"fast {B},{Hq},{Hkv},{Nq},{Nk},{d},{causal},{R}")
+    assert np.abs(l.cpu().numpy() - rl).max() < 5e-3
+    ex, _ = oatt.qk4v8_prefill(q, k, v, scale, causal, R)
+    rel = np.linalg.norm(got - ex) / np.linalg.norm(ex)
+    print(f"[report] fast mode vs exact attention of the quantized operands: rel_l2={rel:.3e}", flush=True)
+
+
+def test_prefill_fast_mode_workload_sample(gpu):
+    """The causal GQA workload in fast mode, sampled rows of batch 0."""
+    from bit_quantized_attention_online_amd import ops
+    w = synth.WORKLOADS[2]
+    q, k, v = synth.prefill_inputs(2)
+    scale = 1.0 / math.sqrt(w["d"])
+    o = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=True, softmax_scale=scale,
+                         v_tile_rows=w["v_tile_rows"], p_terms=1)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, w["Nq"], 97), [w["Nq"] - 1]]))
+    ro, _ = oatt.qk4v8_prefill_fast(q[:1, :, rows], k[:1], v[:1], scale, True, w["v_tile_rows"],
+                                    rows=(rows, w["Nq"]))
+    sel = torch.from_numpy(rows).to(o.device)
+    assert_attn_close(from_dev_bf16(o[:1].index_select(2, sel)), ro, "fast workload 2 batch 0 sampled rows")

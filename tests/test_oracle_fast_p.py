@@ -1,0 +1,70 @@
+"""Pins for the oracle's single-term FP8 probability attention
+(``attention.attention_fast_p``): an independent scalar route, weights that are
+exact powers of two (then it equals exact attention), invariances, and the
+E4M3 error bound against exact attention."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import scalar
+
+
+@pytest.mark.parametrize("nq,nk,causal", [(5, 9, False), (4, 7, True), (3, 300, True), (2, 260, False)])
+def test_fast_p_vs_scalar_brute_force(nq, nk, causal):
+    rng = np.random.default_rng(nq * 100 + nk)
+    d = 8
+    q = rng.standard_normal((nq, d)) * 2.0
+    k = rng.standard_normal((nk, d))
+    v = rng.standard_normal((nk, d))
+    sigma = float(np.float32(0.7))
+    o, lse = A.attention_fast_p(q[None, None], k[None, None], v[None, None], 0.7, causal)
+    ro, rl = scalar.attention_rows_fast_p(q.tolist(), k.tolist(), v.tolist(), sigma, causal)
+    assert np.allclose(o[0, 0], np.array(ro), rtol=0, atol=1e-12)
+    assert np.allclose(lse[0, 0], np.array(rl), rtol=0, atol=1e-12)
+
+
+def test_power_of_two_weights_give_exact_attention():
+    # one-hot keys and log2-domain scores that are integers: every weight is a
+    # power of two within E4M3's range, so the rounding is exact
+    rng = np.random.default_rng(1)
+    nk, nq = 20, 6
+    k = np.eye(nk)
+    n = rng.integers(-6, 1, size=(nq, nk)).astype(np.float64)
+    q = n * math.log(2.0)
+    v = rng.standard_normal((nk, nk))
+    o, lse = A.attention_fast_p(q[None, None], k[None, None], v[None, None], 1.0, False)
+    ro, rl = A.attention(q[None, None], k[None, None], v[None, None], 1.0, False)
+    assert np.allclose(o, ro, rtol=0, atol=1e-12)
+    assert np.allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+def test_constant_v_and_within_block_permutation():
+    rng = np.random.default_rng(2)
+    nk, d = 256, 16
+    q = rng.standard_normal((1, 1, 3, d))
+    k = rng.standard_normal((1, 1, nk, d))
+    v = np.tile(rng.standard_normal(d), (nk, 1))[None, None]
+    o, _ = A.attention_fast_p(q, k, v, 0.3, False)
+    assert np.allclose(o, v[:, :, :3], rtol=0, atol=1e-12)
+    # permuting keys inside each 128-key block leaves the result unchanged
+    v = rng.standard_normal((1, 1, nk, d))
+    perm = np.concatenate([rng.permutation(128), 128 + rng.permutation(128)])
+    o1, l1 = A.attention_fast_p(q, k, v, 0.3, False)
+    o2, l2 = A.attention_fast_p(q, k[:, :, perm], v[:, :, perm], 0.3, False)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12) and np.allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def test_error_bound_against_exact():
+    # every weight carries a relative rounding error of at most 2^-4 (E4M3 has
+    # 3 mantissa bits) unless it is below the block's subnormal range; so the
+    # output moves by at most about 2 * 2^-4 * max|v|
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 2, 64, 32))
+    k = rng.standard_normal((1, 2, 400, 32))
+    v = rng.standard_normal((1, 2, 400, 32))
+    o, _ = A.attention_fast_p(q, k, v, 0.2, True)
+    ro, _ = A.attention(q, k, v, 0.2, True)
+    assert np.abs(o - ro).max() <= 2 * 2.0 ** -4 * np.abs(v).max()
+    assert np.abs(o - ro).max() > 0          # the rounding is really applied
