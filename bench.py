@@ -122,8 +122,28 @@ def bench_prefill(torch, ops, synth, steps, warmup):
     torch.cuda.synchronize()
     fast_ms = sum(e.ms(0, 1) for e in evf) / steps
     assert torch.isfinite(ppf.o.float()).all().item(), "non-finite fast-mode output"
+    del ppf
+    # Hadamard-rotated Q and K: the whole step (the rotation sits in the K
+    # pack and in the attention kernel's Q prologue)
+    pph = ops.PackedPrefill(qd, kd, vd, causal=True, softmax_scale=1.0 / math.sqrt(w["d"]),
+                            v_tile_rows=w["v_tile_rows"], hadamard=True)
+    settle(torch, lambda: (pph.pack(), pph.attend()), seconds=0.2)
+    for _ in range(warmup):
+        pph.pack()
+        pph.attend()
+    evh = [Events(torch, 3) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evh:
+        e.record(0, stream)
+        pph.pack(stream)
+        e.record(1, stream)
+        pph.attend(stream)
+        e.record(2, stream)
+    torch.cuda.synchronize()
+    had = dict(pack_ms=sum(e.ms(0, 1) for e in evh) / steps, attn_ms=sum(e.ms(1, 2) for e in evh) / steps)
+    assert torch.isfinite(pph.o.float()).all().item(), "non-finite rotated output"
     return dict(w=w, wall_ms=wall * 1e3 / steps, pack_ms=pack_ms, attn_ms=attn_ms, flops=flops, pairs=pairs,
-                fast_ms=fast_ms)
+                fast_ms=fast_ms, had=had)
 
 
 def build_cache(torch, ops, w, seed):
@@ -326,6 +346,10 @@ def main():
                                                           / PEAK_MIXED_TFLOPS, 4),
                               "note": "single-term E4M3 probabilities; about 2e-2 relative L2 from exact attention, "
                                       "outside the 5e-3 gate of the default path"},
+        "prefill_hadamard": {"hadamard": 1, "pack_kv_ms": round(pf["had"]["pack_ms"], 4),
+                             "attention_ms": round(pf["had"]["attn_ms"], 4),
+                             "value": round(pf["flops"] / ((pf["had"]["pack_ms"] + pf["had"]["attn_ms"]) * 1e-3)
+                                            / 1e12, 1), "unit": "TFLOP/s"},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel<128,causal>",
                      "achieved": round(attn_tflops, 1), "peak": round(PEAK_MIXED_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_MIXED_TFLOPS, 4), "traffic": traffic},

@@ -51,7 +51,23 @@ __device__ __forceinline__ void append_k(const AppendParams& p, int64_t id, int6
     w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
   }
   uint32_t codes[4];
-  const uint32_t scale = mxfp4_quantize32(w, codes);
+  uint32_t scale;
+  if (!p.hadamard) {
+    scale = mxfp4_quantize32(w, codes);
+  } else {
+    // rotated K rows: the NB threads of a row are adjacent lanes (g fastest),
+    // and every exit above is taken by whole rows, so the pairs are complete
+    float x[32];
+    unpack_bf16x32(w, x);
+    fwht32(x);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = hadamard_pair(x[i], __shfl_xor(x[i], 1, 64), (g & 1) != 0);
+    if constexpr (NB == 4) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = hadamard_pair(x[i], __shfl_xor(x[i], 2, 64), (g & 2) != 0);
+    }
+    scale = mxfp4_quantize32f(x, codes);
+  }
   const int64_t row = ((int64_t)b * p.kv_heads + h) * p.cap + len + t;
   *reinterpret_cast<uint4*>(p.k_codes + row * (D / 2) + 16 * g) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
   p.k_scales[row * NB + g] = (uint8_t)scale;

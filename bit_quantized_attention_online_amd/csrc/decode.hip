@@ -46,7 +46,8 @@ struct DecodeArgs {
   int64_t qs0, qs1, qs2;
   int kv_heads, group, q_len, M, kv_len, cap, R, splits, tiles_per_split;
   int64_t n_vtiles_cap;
-  float c;
+  float c;          // softmax_scale * log2(e), divided by D for rotated queries
+  int hadamard;
 };
 
 template <int D>
@@ -91,21 +92,32 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
   const int qt = row_ok ? mrow / a.group : 0;
   const int head = kvh * a.group + (row_ok ? mrow - qt * a.group : 0);
   const int lim = row_ok ? kvlen - a.q_len + qt : -1;   // last visible key
-  uint4 qc = make_uint4(0, 0, 0, 0);
-  int qsc = 127;
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = 0;
   if (row_ok && lg < NB) {
     const uint4* src = reinterpret_cast<const uint4*>(a.q + b * a.qs0 + qt * a.qs1 + (int64_t)head * a.qs2 + 32 * lg);
-    uint32_t w[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 x = src[i];
       w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
     }
-    uint32_t cq[4];
-    qsc = (int)mxfp4_quantize32(w, cq);
-    qc = make_uint4(cq[0], cq[1], cq[2], cq[3]);
   }
-  const v8i qf = fp4_operand(qc);
+  uint32_t cq[4] = {0, 0, 0, 0};
+  int qsc = 127;
+  if (!a.hadamard) {
+    if (row_ok && lg < NB) qsc = (int)mxfp4_quantize32(w, cq);
+  } else {
+    // rotated queries: lane (q, g) holds block g, so stage 32 pairs lanes
+    // l and l ^ 16 and stage 64 lanes l and l ^ 32
+    float x[32];
+    unpack_bf16x32(w, x);
+    fwht32(x);
+    hadamard_stage_lane_xor16(x, (lg & 1) != 0);
+    if constexpr (NB == 4) hadamard_stage_lane_xor32(x, (lg & 2) != 0);
+    if (row_ok && lg < NB) qsc = (int)mxfp4_quantize32f(x, cq);
+  }
+  const v8i qf = fp4_operand(make_uint4(cq[0], cq[1], cq[2], cq[3]));
 
   v4f O[ND];
 #pragma unroll
@@ -314,7 +326,8 @@ static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   a.kv_heads = p.kv_heads; a.group = G; a.q_len = p.q_len; a.M = M; a.kv_len = p.kv_len; a.cap = p.cap;
   a.R = p.v_tile_rows; a.splits = splits; a.tiles_per_split = (tiles + splits - 1) / splits;
   a.n_vtiles_cap = (p.cap + p.v_tile_rows - 1) / p.v_tile_rows;
-  a.c = p.softmax_scale * kLog2e;
+  a.c = p.softmax_scale * kLog2e / (p.hadamard ? (float)D : 1.0f);
+  a.hadamard = p.hadamard;
   const dim3 grid((unsigned)((int64_t)p.batch * p.kv_heads * splits));
   const int MB = (M + 15) / 16;
   switch (MB) {

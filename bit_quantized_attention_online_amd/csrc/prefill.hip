@@ -133,7 +133,7 @@ PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, i
 template <int D>
 __global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict__ k, int64_t ks0, int64_t ks1,
                                                      int64_t ks2, int kv_heads, int seq_k, int64_t n_tiles,
-                                                     uint8_t* __restrict__ rec, int64_t total) {
+                                                     uint8_t* __restrict__ rec, int64_t total, int hadamard) {
   using TB = TileBytes<D>;
   constexpr int NB = D / 32, NS = D / 64;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -150,15 +150,32 @@ __global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict_
   const int step = g >> 1, lane = rho + 32 * (g & 1);
   uint32_t codes[4] = {0, 0, 0, 0};
   uint32_t scale = 127;
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = 0;
   if (jj < seq_k) {
     const uint4* src = reinterpret_cast<const uint4*>(k + b * ks0 + h * ks1 + jj * ks2 + 32 * g);
-    uint32_t w[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 x = src[q];
       w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
     }
-    scale = mxfp4_quantize32(w, codes);
+  }
+  if (!hadamard) {
+    if (jj < seq_k) scale = mxfp4_quantize32(w, codes);
+  } else {
+    // the NB threads of a key row are adjacent lanes (g fastest): stage 32
+    // pairs lanes ^ 1, stage 64 lanes ^ 2
+    float x[32];
+    unpack_bf16x32(w, x);
+    fwht32(x);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = hadamard_pair(x[i], __shfl_xor(x[i], 1, 64), (g & 1) != 0);
+    if constexpr (NB == 4) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = hadamard_pair(x[i], __shfl_xor(x[i], 2, 64), (g & 2) != 0);
+    }
+    if (jj < seq_k) scale = mxfp4_quantize32f(x, codes);
   }
   uint8_t* r = rec + (bk * n_tiles + tile) * TB::REC;
   *reinterpret_cast<uint4*>(r + (kb * NS + step) * 1024 + lane * 16) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
@@ -275,7 +292,8 @@ struct AttnArgs {
   int q_heads, kv_heads, group, heads_per_wg, pos_blocks, seq_q, seq_k;
   int xblocks, pos_groups;   // 1-D grid = pos_groups x xblocks, xblocks fastest
   int64_t n_tiles;
-  float c;          // softmax_scale * log2(e)
+  float c;          // softmax_scale * log2(e), divided by D for rotated Q/K
+  int hadamard;     // Q (and the packed K) rotated by H_D
 };
 
 // Ping-pong schedule.  The 8 waves form two groups of 4 (one wave of each on
@@ -342,24 +360,55 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // holds head_dim block 2s + h of row q for contraction step s ----
   v8i qf[NS];
   int qsc[NS];
+  {
+    uint32_t w[NS][16];
 #pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    uint4 qc = make_uint4(0, 0, 0, 0);
-    qsc[st] = 127;
-    if (row < a.seq_q) {
-      const uint4* src =
-          reinterpret_cast<const uint4*>(a.q + b * a.qs0 + (int64_t)head * a.qs1 + row * a.qs2 + 32 * (2 * st + lh));
-      uint32_t w[16];
+    for (int st = 0; st < NS; ++st) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 x = src[i];
-        w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+      for (int i = 0; i < 16; ++i) w[st][i] = 0;
+      if (row < a.seq_q) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.q + b * a.qs0 + (int64_t)head * a.qs1 + row * a.qs2 +
+                                                          32 * (2 * st + lh));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 x = src[i];
+          w[st][4 * i] = x.x; w[st][4 * i + 1] = x.y; w[st][4 * i + 2] = x.z; w[st][4 * i + 3] = x.w;
+        }
       }
-      uint32_t c[4];
-      qsc[st] = (int)mxfp4_quantize32(w, c);
-      qc = make_uint4(c[0], c[1], c[2], c[3]);
     }
-    qf[st] = fp4_operand(qc);
+    if (!a.hadamard) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        uint32_t c[4] = {0, 0, 0, 0};
+        qsc[st] = row < a.seq_q ? (int)mxfp4_quantize32(w[st], c) : 127;
+        qf[st] = fp4_operand(v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]});
+      }
+    } else {
+      // rotated rows: lane (q, h) holds blocks h (step 0) and 2 + h (step 1),
+      // so stage 32 pairs the lane with lane ^ 32 and stage 64 pairs its two
+      // steps
+      float x[NS][32];
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        unpack_bf16x32(w[st], x[st]);
+        fwht32(x[st]);
+        hadamard_stage_lane_xor32(x[st], lh == 1);
+      }
+      if constexpr (NS == 2) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float u = x[0][i], v = x[1][i];
+          x[0][i] = u + v;
+          x[1][i] = u - v;
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        uint32_t c[4];
+        qsc[st] = (int)mxfp4_quantize32f(x[st], c);
+        qf[st] = fp4_operand(v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]});
+      }
+    }
   }
 
   v16f O[NDB];
@@ -566,7 +615,8 @@ static hipError_t launch_pack_d(const PrefillParams& p, hipStream_t stream) {
   const int64_t bk = (int64_t)p.batch * p.kv_heads;
   const int64_t total_k = bk * L.n_tiles * kKvTile * (D / 32);
   hipLaunchKernelGGL((pack_k_kernel<D>), dim3((unsigned)((total_k + 255) / 256)), dim3(256), 0, stream, p.k,
-                     p.ks[0], p.ks[1], p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, p.ws + L.off_rec, total_k);
+                     p.ks[0], p.ks[1], p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, p.ws + L.off_rec, total_k,
+                     p.hadamard);
   hipLaunchKernelGGL((vtile_scale_kernel<D>), dim3((unsigned)(bk * L.n_vtiles)), dim3(256), 0, stream, p.v,
                      p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_vtiles, wvt);
   hipLaunchKernelGGL((pack_v_kernel<D>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v, p.vs[0],
@@ -589,7 +639,10 @@ static hipError_t launch_attn_d(const PrefillParams& p, hipStream_t stream) {
   a.pos_blocks = kWaves / a.heads_per_wg;
   a.seq_q = p.seq_q; a.seq_k = p.seq_k;
   a.n_tiles = L.n_tiles;
-  a.c = p.softmax_scale * kLog2e;
+  // rotated rows: (H q).(H k) = D (q.k), so the score multiplier is divided
+  // by D (exact: a power of two)
+  a.c = p.softmax_scale * kLog2e / (p.hadamard ? (float)D : 1.0f);
+  a.hadamard = p.hadamard;
   const int rows_per_wg = a.pos_blocks * kRowsPerWave;
   a.xblocks = p.batch * p.kv_heads * (a.group / a.heads_per_wg);
   a.pos_groups = (p.seq_q + rows_per_wg - 1) / rows_per_wg;

@@ -52,6 +52,7 @@ qk4v8_status validate_prefill(const qk4v8_prefill_args* a) {
   if (!good_scale(a->softmax_scale)) return QK4V8_ERR_SHAPE;
   if (a->seq_q > (1 << 30) || a->seq_k > (1 << 30)) return QK4V8_ERR_SHAPE;
   if (a->p_terms != 0 && a->p_terms != 1 && a->p_terms != 2) return QK4V8_ERR_SHAPE;
+  if (a->hadamard != 0 && a->hadamard != 1) return QK4V8_ERR_SHAPE;
   return QK4V8_OK;
 }
 
@@ -84,6 +85,7 @@ qk4v8_status validate_decode(const qk4v8_decode_args* a) {
   if ((int64_t)(a->q_heads / a->kv_heads) * a->q_len > 64) return QK4V8_ERR_SHAPE;
   if (a->num_splits < 0) return QK4V8_ERR_SHAPE;
   if (!good_scale(a->softmax_scale)) return QK4V8_ERR_SHAPE;
+  if (a->hadamard != 0 && a->hadamard != 1) return QK4V8_ERR_SHAPE;
   return QK4V8_OK;
 }
 
@@ -183,6 +185,7 @@ qk4v8_status run_prefill(const qk4v8_prefill_args* a, hipStream_t stream, int pa
   p.batch = a->batch; p.q_heads = a->q_heads; p.kv_heads = a->kv_heads; p.seq_q = a->seq_q; p.seq_k = a->seq_k;
   p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows; p.causal = a->causal;
   p.single_term = a->p_terms == 1;
+  p.hadamard = a->hadamard;
   p.softmax_scale = a->softmax_scale;
   p.ws = static_cast<uint8_t*>(a->workspace);
   if (parts & kPack) {
@@ -221,6 +224,7 @@ qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream) {
   if (!valid_v_tile(a->v_tile_rows)) return QK4V8_ERR_SHAPE;
   if (a->kv_lens == nullptr && (a->kv_len < 0 || (int64_t)a->kv_len + a->n_new > a->cap)) return QK4V8_ERR_SHAPE;
   if (a->cap > (1 << 30)) return QK4V8_ERR_SHAPE;
+  if (a->hadamard != 0 && a->hadamard != 1) return QK4V8_ERR_SHAPE;
   for (int i = 0; i < 3; ++i)
     if (a->k_stride[i] < 0 || a->k_stride[i] % 8 != 0 || a->v_stride[i] < 0 || a->v_stride[i] % 8 != 0)
       return QK4V8_ERR_STRIDE;
@@ -243,7 +247,7 @@ qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream) {
   p.k_codes = a->k_codes; p.k_scales = a->k_scales; p.v_codes = a->v_codes; p.v_scales = a->v_scales;
   p.v_tail = a->v_tail; p.kv_lens = a->kv_lens;
   p.batch = a->batch; p.kv_heads = a->kv_heads; p.n_new = a->n_new; p.kv_len = a->kv_len; p.cap = a->cap;
-  p.head_dim = a->head_dim; p.R = a->v_tile_rows;
+  p.head_dim = a->head_dim; p.R = a->v_tile_rows; p.hadamard = a->hadamard;
   p.n_vtiles_cap = (a->cap + a->v_tile_rows - 1) / a->v_tile_rows;
   return from_hip(launch_append(p, stream));
 }
@@ -263,6 +267,7 @@ qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream) {
   p.batch = a->batch; p.q_len = a->q_len; p.q_heads = a->q_heads; p.kv_heads = a->kv_heads; p.kv_len = a->kv_len;
   p.cap = a->cap; p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows;
   p.num_splits = a->num_splits; p.softmax_scale = a->softmax_scale;
+  p.hadamard = a->hadamard;
   p.ws = static_cast<uint8_t*>(a->workspace);
   return from_hip(launch_decode(p, stream));
 }

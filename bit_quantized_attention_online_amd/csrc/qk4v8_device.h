@@ -110,6 +110,83 @@ __device__ __forceinline__ uint32_t mxfp4_quantize32(const uint32_t (&w)[16], ui
   return (uint32_t)(X + 127);
 }
 
+// MXFP4 of 32 fp32 values (exact float32 inputs, e.g. rotated rows): the same
+// rule as mxfp4_quantize32 on values that are not bf16.
+__device__ __forceinline__ uint32_t mxfp4_quantize32f(const float (&x)[32], uint32_t (&codes)[4]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const int X = mx_shared_exp(amax, 2);
+  const float inv = exp2i(-X);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c |= e2m1_pack2(x[8 * i + 2 * j] * inv, x[8 * i + 2 * j + 1] * inv) << (8 * j);
+    codes[i] = c;
+  }
+  return (uint32_t)(X + 127);
+}
+
+// 32 bf16 (16 packed dwords, element 2i in the low half of word i) -> fp32.
+__device__ __forceinline__ void unpack_bf16x32(const uint32_t (&w)[16], float (&x)[32]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+// Sylvester-Hadamard transform of head_dim rows ("MpFA免训练量化：QK4V8混合精度在
+// Blackwell上的推理加速实践" §3.1: a rotation spreads outlier channels over
+// all channels before 4-bit quantization).  Butterfly stages h = 1, 2, ...,
+// d/2 in that order, (x_i, x_{i+h}) -> (x_i + x_{i+h}, x_i - x_{i+h}), in
+// fp32; a lane holds one 32-element block, so stages h < 32 run in the lane
+// and stage h = 32 * 2^k pairs the lane with the lane holding block b ^ 2^k.
+__device__ __forceinline__ void fwht32(float (&x)[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+}
+
+// One cross-lane butterfly stage: `partner` is the value the other lane of the
+// pair holds at the same position; the lane with the lower block index keeps
+// the sum, the other the difference (lower - upper).
+__device__ __forceinline__ float hadamard_pair(float own, float partner, bool upper) {
+  return upper ? partner - own : own + partner;
+}
+
+// The partner's value out of a lane-swap result pair (whichever of the two is
+// not this lane's own bits; when both are, the partner holds the same value).
+__device__ __forceinline__ float swap_partner(float own, uint32_t r0, uint32_t r1) {
+  return __uint_as_float(r0 != __float_as_uint(own) ? r0 : r1);
+}
+
+// Stage h = 32 * 2^k with the pair lanes l and l ^ 16 (k chosen by the caller's
+// layout), using v_permlane16_swap.
+__device__ __forceinline__ void hadamard_stage_lane_xor16(float (&x)[32], bool upper) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i]), false, false);
+    x[i] = hadamard_pair(x[i], swap_partner(x[i], r[0], r[1]), upper);
+  }
+}
+
+// The same with the pair lanes l and l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ void hadamard_stage_lane_xor32(float (&x)[32], bool upper) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i]), false, false);
+    x[i] = hadamard_pair(x[i], swap_partner(x[i], r[0], r[1]), upper);
+  }
+}
+
 // Scaled MFMA wrappers.  `sa`/`sb` hold E8M0 bytes; OPA/OPB select the byte.
 template <int FA, int FB, int OPA = 0, int OPB = 0>
 __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {

@@ -34,6 +34,7 @@ struct PrefillParams {
   int64_t qs[3], ks[3], vs[3], os[3];
   int batch, q_heads, kv_heads, seq_q, seq_k, head_dim, v_tile_rows, causal;
   int single_term;           // 1: fast mode (one E4M3 term per probability)
+  int hadamard;              // 1: Q and K rotated by the Sylvester-Hadamard H_d
   float softmax_scale;
   uint8_t* ws;
 };
@@ -51,6 +52,7 @@ struct DecodeParams {
   float* lse;
   int64_t qs[3], os[3];
   int batch, q_len, q_heads, kv_heads, kv_len, cap, head_dim, v_tile_rows, num_splits;
+  int hadamard;              // 1: queries rotated by H_d (the cache K was written rotated)
   float softmax_scale;
   uint8_t* ws;
 };
@@ -71,6 +73,7 @@ struct AppendParams {
   uint16_t* v_tail;          // [batch * kv_heads, R, head_dim]
   const int32_t* kv_lens;
   int batch, kv_heads, n_new, kv_len, cap, head_dim, R;
+  int hadamard;              // 1: K rows rotated by H_d before quantization
   int64_t n_vtiles_cap;      // ceil(cap / R)
 };
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);

@@ -34,7 +34,7 @@ class PrefillArgs(ctypes.Structure):
                 ("v_tile_rows", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("p_terms", ctypes.c_int32)]
+                ("p_terms", ctypes.c_int32), ("hadamard", ctypes.c_int32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -46,7 +46,8 @@ class DecodeArgs(ctypes.Structure):
                 ("kv_heads", ctypes.c_int32), ("kv_len", ctypes.c_int32), ("cap", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("v_tile_rows", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("hadamard", ctypes.c_int32)]
 
 
 class AppendArgs(ctypes.Structure):
@@ -56,7 +57,7 @@ class AppendArgs(ctypes.Structure):
                 ("v_scales", ctypes.c_void_p), ("v_tail", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("n_new", ctypes.c_int32),
                 ("kv_len", ctypes.c_int32), ("cap", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("v_tile_rows", ctypes.c_int32)]
+                ("v_tile_rows", ctypes.c_int32), ("hadamard", ctypes.c_int32)]
 
 
 class QK4V8Error(RuntimeError):
@@ -150,7 +151,7 @@ def quantize_v(v, tile_rows, stream=None):
     return codes, scales
 
 
-def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms=2):
+def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms=2, hadamard=False):
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
     a = PrefillArgs()
@@ -164,6 +165,7 @@ def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms=2
     a.v_tile_rows, a.causal = v_tile_rows, int(bool(causal))
     a.softmax_scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
     a.p_terms = p_terms
+    a.hadamard = int(bool(hadamard))
     return a
 
 
@@ -174,15 +176,16 @@ def prefill_workspace_bytes(q, k, v, causal=False, softmax_scale=None, v_tile_ro
 
 
 def attn_prefill(q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, out=None,
-                 workspace=None, stream=None, p_terms=2):
+                 workspace=None, stream=None, p_terms=2, hadamard=False):
     """QK4V8 prefill.  q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d] bf16 (any strides
     with unit innermost).  Returns o [B, Hq, Nq, d] bf16 (and lse fp32
-    [B, Hq, Nq] when return_lse).  p_terms=1 selects the single-term fast mode."""
+    [B, Hq, Nq] when return_lse).  p_terms=1 selects the single-term fast mode;
+    hadamard=True rotates Q and K by H_d before quantization."""
     for t in (q, k, v):
         _bits16(t)
     o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-    a = _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms)
+    a = _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms, hadamard)
     need = lib().qk4v8_prefill_workspace_bytes(ctypes.byref(a))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -196,12 +199,14 @@ class PackedPrefill:
     ``pack()`` quantizes K/V into the workspace, ``attend()`` runs the
     attention kernel from it (used to time the two halves separately)."""
 
-    def __init__(self, q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, p_terms=2):
+    def __init__(self, q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, p_terms=2,
+                 hadamard=False):
         for t in (q, k, v):
             _bits16(t)
         self.o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
         self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-        self.args = _prefill_args(q, k, v, self.o, self.lse, causal, softmax_scale, v_tile_rows, p_terms)
+        self.args = _prefill_args(q, k, v, self.o, self.lse, causal, softmax_scale, v_tile_rows, p_terms,
+                                  hadamard)
         need = lib().qk4v8_prefill_workspace_bytes(ctypes.byref(self.args))
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self.args.workspace, self.args.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
@@ -245,7 +250,7 @@ def decode_workspace_bytes(q, k_codes, kv_len, v_tile_rows=256, num_splits=0):
 
 
 def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256, kv_lens=None, num_splits=0,
-                softmax_scale=None, return_lse=False, out=None, workspace=None, stream=None):
+                softmax_scale=None, return_lse=False, out=None, workspace=None, stream=None, hadamard=False):
     """QK4V8 decode / block verify over a quantized cache.
     q [B, q_len, Hq, d] bf16; k_codes [B, Hkv, cap, d/2], k_scales [B, Hkv, cap, d/32],
     v_codes [B, Hkv, cap, d], v_scales [B, Hkv, ceil(cap/v_tile_rows)] uint8.
@@ -257,6 +262,7 @@ def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256
         raise TypeError("kv_lens must be int32")
     a = _decode_args(q, k_codes, k_scales, v_codes, v_scales, o, lse, kv_len, v_tile_rows, kv_lens, num_splits,
                      softmax_scale)
+    a.hadamard = int(bool(hadamard))
     need = lib().qk4v8_decode_workspace_bytes(ctypes.byref(a))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -266,7 +272,7 @@ def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256
 
 
 def kv_append(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows=256,
-              kv_lens=None, stream=None):
+              kv_lens=None, stream=None, hadamard=False):
     """Quantize n_new tokens per sequence into a decode cache (in place).
     k_new, v_new [B, n_new, Hkv, d] bf16 (token-major, strided); cache tensors as
     for attn_decode with capacity cap = k_codes.shape[2]; v_tail [B, Hkv, R, d]
@@ -300,4 +306,5 @@ def kv_append(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len
     a.kv_lens = kv_lens.data_ptr() if kv_lens is not None else None
     a.batch, a.kv_heads, a.n_new, a.kv_len = B, Hkv, n_new, int(kv_len)
     a.cap, a.head_dim, a.v_tile_rows = k_codes.shape[2], d, v_tile_rows
+    a.hadamard = int(bool(hadamard))
     _check(lib().qk4v8_kv_append(ctypes.byref(a), _stream(stream)), "qk4v8_kv_append")

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QK4V8_ABI_VERSION 3
+#define QK4V8_ABI_VERSION 4
 
 typedef enum {
   QK4V8_OK = 0,
@@ -141,6 +141,14 @@ qk4v8_status qk4v8_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int3
  *               t = s*log2(e) and 128-key blocks B aligned at multiples of 128,
  *               p~_j = 2^X_B * E4M3(2^(t_j - X_B)), X_B = floor(max_B t) - 7, and
  *               o = sum_j p~_j v_j / sum_j p~_j.
+ *   hadamard  : 1 rotates every Q and K row by the Sylvester-Hadamard matrix
+ *               H_d (+-1 entries, H_2n = [[H_n, H_n], [H_n, -H_n]]) before its
+ *               MXFP4 quantization (MpFA page §3.1: a rotation spreads outlier
+ *               channels over all channels).  The rotation is evaluated in fp32
+ *               with the butterfly stages h = 1, 2, ..., d/2 in that order, and
+ *               the scores are multiplied by softmax_scale / d, since
+ *               (H q).(H k) = d (q.k): exact attention is unchanged and only
+ *               the quantization error moves.  0: no rotation.
  */
 typedef struct {
   const uint16_t* q;
@@ -157,6 +165,7 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   int32_t p_terms;
+  int32_t hadamard;
 } qk4v8_prefill_args;
 
 /* Workspace bytes qk4v8_attn_prefill needs for these sizes (0 on bad sizes). */
@@ -201,6 +210,10 @@ qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t 
  *   num_splits: KV splits per (batch, kv-head), 0 = chosen by the library.
  *   workspace : at least qk4v8_decode_workspace_bytes() bytes, 256-byte aligned
  *               (fp32 partial outputs and log-sum-exps of the splits).
+ *   hadamard  : 1 when the cache's K rows were rotated before quantization
+ *               (qk4v8_kv_append with hadamard = 1); the queries are then
+ *               rotated the same way and the scores multiplied by
+ *               softmax_scale / head_dim (see qk4v8_prefill_args).  0: neither.
  */
 typedef struct {
   const uint16_t* q;
@@ -217,6 +230,7 @@ typedef struct {
   float softmax_scale;
   void* workspace;
   size_t workspace_bytes;
+  int32_t hadamard;
 } qk4v8_decode_args;
 
 /* Workspace bytes qk4v8_attn_decode needs for these sizes (0 on bad sizes). */
@@ -250,6 +264,8 @@ qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream);
  *                  append left it; nothing is needed when len_b % R == 0).
  *   head_dim ∈ {64, 128}; v_tile_rows ∈ {32, 64, 128, 256}; n_new >= 0 (0 is a
  *   no-op); with kv_lens NULL, 0 <= kv_len and kv_len + n_new <= cap.
+ *   hadamard     : 1 rotates the new K rows by H_d before quantization (for a
+ *                  cache read by qk4v8_attn_decode with hadamard = 1); 0: not.
  */
 typedef struct {
   const uint16_t* k_new;
@@ -263,6 +279,7 @@ typedef struct {
   uint16_t* v_tail;
   const int32_t* kv_lens;
   int32_t batch, kv_heads, n_new, kv_len, cap, head_dim, v_tile_rows;
+  int32_t hadamard;
 } qk4v8_append_args;
 
 qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream);

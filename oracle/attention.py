@@ -23,7 +23,7 @@ bottom-right mask.
 import numpy as np
 
 from .formats import e4m3_decode, e4m3_encode
-from .quant import dequantize_qk, dequantize_v, quantize_qk, quantize_v
+from .quant import dequantize_qk, dequantize_v, quantize_qk, quantize_qk_hadamard, quantize_v
 
 _CHUNK_ELEMS = 1 << 25
 
@@ -212,3 +212,38 @@ def qk4v8_prefill_fast(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_row
     vc, vs = quantize_v(v_bits.reshape(B * Hkv, Nk, d), v_tile_rows)
     vh = dequantize_v(vc, vs, v_tile_rows).reshape(B, Hkv, Nk, d)
     return attention_fast_p(qh, kh, vh, softmax_scale, causal, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# Hadamard-rotated Q and K (MpFA page §3.1).  Q and K rows are rotated by the
+# Sylvester-Hadamard matrix H_d (``quant.hadamard_rows_f32``) before MXFP4;
+# since (H q).(H k) = d (q.k), the scores are scaled by softmax_scale / d
+# (exact: d is a power of two).  V is unchanged.
+# ---------------------------------------------------------------------------
+
+def qk4v8_prefill_hadamard(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_rows, rows=None):
+    """``qk4v8_prefill`` with rotated Q and K."""
+    d = q_bits.shape[-1]
+    qh = dequantize_qk(*quantize_qk_hadamard(q_bits))
+    kh = dequantize_qk(*quantize_qk_hadamard(k_bits))
+    B, Hkv, Nk, _ = v_bits.shape
+    vc, vs = quantize_v(v_bits.reshape(B * Hkv, Nk, d), v_tile_rows)
+    vh = dequantize_v(vc, vs, v_tile_rows).reshape(B, Hkv, Nk, d)
+    return attention(qh, kh, vh, float(np.float32(softmax_scale)) / d, causal, rows=rows)
+
+
+def qk4v8_decode_hadamard(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens, v_tile_rows, softmax_scale):
+    """``qk4v8_decode`` over a cache whose K rows were rotated before
+    quantization; the queries are rotated the same way."""
+    B, q_len, Hq, d = q_bits.shape
+    qh = dequantize_qk(*quantize_qk_hadamard(q_bits)).transpose(0, 2, 1, 3)
+    o = np.zeros((B, q_len, Hq, d))
+    lse = np.zeros((B, q_len, Hq))
+    for b in range(B):
+        n = int(kv_lens[b])
+        kh = dequantize_qk(k_codes[b, :, :n], k_scales[b, :, :n])
+        vh = dequantize_v(v_codes[b, :, :n], v_scales[b], v_tile_rows)
+        ob, lb = attention(qh[b:b + 1], kh[None], vh[None], float(np.float32(softmax_scale)) / d, causal=True)
+        o[b] = ob[0].transpose(1, 0, 2)
+        lse[b] = lb[0].T
+    return o, lse

@@ -42,7 +42,13 @@ def quantize_qk(x_bits):
     row holds element 2k in its low nibble and element 2k+1 in its high
     nibble; a scale byte is X + 127.
     """
-    x = bf16_bits_to_float64(x_bits)
+    return quantize_qk_values(bf16_bits_to_float64(x_bits))
+
+
+def quantize_qk_values(x):
+    """``quantize_qk`` of rows given as float64 values (here: exact float32
+    values, e.g. rotated rows)."""
+    x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     assert d % MX_BLOCK == 0
     blocks = x.reshape(x.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
@@ -96,3 +102,29 @@ def dequantize_v(codes, scales, tile_rows):
     g, n, d = codes.shape
     row_scale = e8m0_decode(scales)[:, np.arange(n) // tile_rows]   # [g, n]
     return e4m3_decode(codes) * row_scale[:, :, None]
+
+
+def hadamard_rows_f32(x_bits):
+    """Sylvester-Hadamard transform y = H_d x of bf16 rows along the last axis
+    (d a power of two; H has +-1 entries, H_2n = [[H_n, H_n], [H_n, -H_n]]),
+    evaluated in float32 with the butterfly stages in the order h = 1, 2, 4,
+    ..., d/2: (x_i, x_{i+h}) -> (x_i + x_{i+h}, x_i - x_{i+h}) for i & h == 0.
+    Every float32 operation is fixed by this order, so the result is exact to
+    the bit.  MpFA page §3.1: a rotation spreads the energy of outlier
+    channels over all channels before the 4-bit quantization; H H^T = d I, so
+    (H q).(H k) = d (q.k) and only the quantization error changes."""
+    x = bf16_bits_to_float64(x_bits).astype(np.float32)
+    d = x.shape[-1]
+    assert d > 0 and d & (d - 1) == 0
+    h = 1
+    while h < d:
+        y = x.reshape(x.shape[:-1] + (d // (2 * h), 2, h))
+        a, b = y[..., 0, :], y[..., 1, :]
+        x = np.stack([a + b, a - b], axis=-2).reshape(x.shape)
+        h *= 2
+    return x
+
+
+def quantize_qk_hadamard(x_bits):
+    """MXFP4 of the rotated rows H_d x (``hadamard_rows_f32``)."""
+    return quantize_qk_values(hadamard_rows_f32(x_bits).astype(np.float64))

@@ -123,3 +123,23 @@ def attention_rows_fast_p(q, k, v, sigma, causal, block=128, headroom=7):
         out.append([math.fsum(p[j] * v[j][c] for j in range(len(p))) / l for c in range(len(v[0]))])
         lses.append((Mi + math.log2(l)) * math.log(2.0))
     return out, lses
+
+
+def _f32(x):
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def hadamard_row_f32(values):
+    """One row through the Sylvester-Hadamard butterflies h = 1, 2, ..., d/2,
+    each sum and difference rounded to float32 by packing (a second route to
+    ``quant.hadamard_rows_f32``)."""
+    x = [_f32(v) for v in values]
+    d = len(x)
+    h = 1
+    while h < d:
+        for i in range(d):
+            if i & h == 0:
+                a, b = x[i], x[i + h]
+                x[i], x[i + h] = _f32(a + b), _f32(a - b)
+        h *= 2
+    return x

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.qk4v8_abi_version() == 3
+    assert L.qk4v8_abi_version() == 4
     for s in range(7):
         assert L.qk4v8_status_string(s)
 
@@ -67,7 +67,7 @@ def _prefill(**kw):
     (dict(causal=2), 2), (dict(seq_q=65), 2), (dict(softmax_scale=0.0), 2), (dict(softmax_scale=float("nan")), 2),
     (dict(q=None), 1), (dict(q_stride=[64 * 128, 128, 36]), 3), (dict(o_stride=[64 * 128, 128, 4]), 3),
     (dict(k=4100), 3), (dict(workspace=None), 5), (dict(workspace=1 << 20 | 8), 5), (dict(workspace_bytes=16), 5),
-    (dict(p_terms=3), 2),
+    (dict(p_terms=3), 2), (dict(hadamard=2), 2),
 ])
 def test_prefill_validation(kw, status):
     a = _prefill(**kw)
@@ -147,6 +147,7 @@ def _append(**kw):
     (dict(k_new=0), 1),
     (dict(v_codes=4100), 3),                   # not 8-byte aligned
     (dict(k_codes=4104), 3),                   # not 16-byte aligned
+    (dict(hadamard=-1), 2),
     (dict(n_new=0), 0),                        # no-op
     (dict(batch=0), 0),
 ])

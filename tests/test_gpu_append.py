@@ -130,3 +130,31 @@ def test_append_strided_inputs_and_decode(gpu):
     assert torch.isfinite(o1.float()).all()
     assert torch.equal(o1, o2)
     print("[parity] append + decode equals one-shot quantization + decode", flush=True)
+
+
+@pytest.mark.parametrize("d,R", [(128, 256), (64, 64)])
+def test_append_hadamard_rotated_k_is_bit_exact(gpu, d, R):
+    """K rows rotated by H_d in fp32 (fixed butterfly order) before MXFP4: the
+    cache codes equal the oracle's to the bit."""
+    from bit_quantized_attention_online_amd import ops
+    B, Hkv, cap = 2, 3, 300
+    k_bits, v_bits = _sequences(B, cap, Hkv, d, seed=d + 5)
+    dev = torch.device("cuda:0")
+    kc = torch.zeros((B, Hkv, cap, d // 2), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((B, Hkv, cap, d // 32), dtype=torch.uint8, device=dev)
+    vc = torch.zeros((B, Hkv, cap, d), dtype=torch.uint8, device=dev)
+    vs = torch.zeros((B, Hkv, -(-cap // R)), dtype=torch.uint8, device=dev)
+    tail = torch.zeros((B, Hkv, R, d), dtype=torch.bfloat16, device=dev)
+    n = 0
+    for c in (1, 77, 150, 2):
+        ops.kv_append(to_dev(k_bits[:, n:n + c]), to_dev(v_bits[:, n:n + c]), kc, ks, vc, vs, tail, n,
+                      v_tile_rows=R, hadamard=True)
+        n += c
+    torch.cuda.synchronize()
+    kcn, ksn, vcn, vsn = (t.cpu().numpy() for t in (kc, ks, vc, vs))
+    for b in range(B):
+        for h in range(Hkv):
+            rkc, rks, rvc, rvs = ocache.cache_of_sequence(k_bits[b, :n, h], v_bits[b, :n, h], R, hadamard=True)
+            assert np.array_equal(kcn[b, h, :n], rkc) and np.array_equal(ksn[b, h, :n], rks), (b, h)
+            assert np.array_equal(vcn[b, h, :n], rvc) and np.array_equal(vsn[b, h, :len(rvs)], rvs), (b, h)
+    print(f"[parity] rotated K append d{d}: bit-exact", flush=True)

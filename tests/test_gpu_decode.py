@@ -130,3 +130,36 @@ def test_decode_workloads_full_size_sampled(gpu, cfg):
         ro, _ = oatt.qk4v8_decode(q[b:b + 1], rkc[None], rks[None], rvc[None], rvs[None],
                                   np.array([w["kv_len"]]), w["v_tile_rows"], 1 / math.sqrt(w["d"]))
         assert_attn_close(o[b:b + 1], ro, f"workload {cfg} batch {b}")
+
+
+@pytest.mark.parametrize("q_len,d", [(1, 128), (4, 128), (2, 64)])
+def test_decode_hadamard(gpu, q_len, d):
+    """Decode over a cache written with rotated K rows, queries rotated in the
+    kernel, against the oracle's rotated definition."""
+    from bit_quantized_attention_online_amd import ops
+    from oracle import cache as ocache
+    B, Hq, Hkv, n, R = 2, 8, 2, 700, 256
+    rng = np.random.default_rng(q_len * 10 + d)
+    k = synth.bf16_bits(rng.standard_normal((B, n, Hkv, d)).astype(np.float32))
+    v = synth.bf16_bits(rng.standard_normal((B, n, Hkv, d)).astype(np.float32))
+    q = synth.bf16_bits(rng.standard_normal((B, q_len, Hq, d)).astype(np.float32))
+    dev = torch.device("cuda:0")
+    kc = torch.zeros((B, Hkv, n, d // 2), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((B, Hkv, n, d // 32), dtype=torch.uint8, device=dev)
+    vc = torch.zeros((B, Hkv, n, d), dtype=torch.uint8, device=dev)
+    vs = torch.zeros((B, Hkv, -(-n // R)), dtype=torch.uint8, device=dev)
+    tail = torch.zeros((B, Hkv, R, d), dtype=torch.bfloat16, device=dev)
+    ops.kv_append(to_dev(k), to_dev(v), kc, ks, vc, vs, tail, 0, v_tile_rows=R, hadamard=True)
+    o, l = ops.attn_decode(to_dev(q), kc, ks, vc, vs, n, v_tile_rows=R, return_lse=True, hadamard=True)
+    torch.cuda.synchronize()
+    rk = np.zeros((B, Hkv, n, d // 2), np.uint8)
+    rks = np.zeros((B, Hkv, n, d // 32), np.uint8)
+    rv = np.zeros((B, Hkv, n, d), np.uint8)
+    rvs = np.zeros((B, Hkv, -(-n // R)), np.uint8)
+    for b in range(B):
+        for h in range(Hkv):
+            rk[b, h], rks[b, h], rv[b, h], rvs[b, h] = ocache.cache_of_sequence(k[b, :, h], v[b, :, h], R, hadamard=True)
+    assert np.array_equal(kc.cpu().numpy(), rk) and np.array_equal(ks.cpu().numpy(), rks)
+    ro, rl = oatt.qk4v8_decode_hadamard(q, rk, rks, rv, rvs, np.array([n] * B), R, 1 / math.sqrt(d))
+    assert_attn_close(from_dev_bf16(o), ro, f"decode hadamard q_len{q_len} d{d}")
+    assert np.abs(l.cpu().numpy() - rl).max() < 5e-3

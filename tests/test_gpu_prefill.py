@@ -167,3 +167,48 @@ def test_prefill_fast_mode_workload_sample(gpu):
                                     rows=(rows, w["Nq"]))
     sel = torch.from_numpy(rows).to(o.device)
     assert_attn_close(from_dev_bf16(o[:1].index_select(2, sel)), ro, "fast workload 2 batch 0 sampled rows")
+
+
+HAD_CASES = [
+    (1, 1, 1, 256, 256, 64, False, 64),
+    (2, 4, 2, 300, 300, 128, True, 64),
+    (1, 8, 1, 77, 333, 128, True, 32),
+    (1, 4, 4, 513, 700, 128, False, 256),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,R", HAD_CASES)
+def test_prefill_hadamard(gpu, B, Hq, Hkv, Nq, Nk, d, causal, R):
+    from bit_quantized_attention_online_amd import ops
+    q, k, v = _inputs(B, Hq, Hkv, Nq, Nk, d, seed=B * 1000 + Nq + Nk + d + 11)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[case] prefill hadamard q{q.shape} k{k.shape} causal={causal} R={R}", flush=True)
+    o, l = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=causal, softmax_scale=scale, v_tile_rows=R,
+                            return_lse=True, hadamard=True)
+    torch.cuda.synchronize()
+    ro, rl = oatt.qk4v8_prefill_hadamard(q, k, v, scale, causal, R)
+    assert_attn_close(from_dev_bf16(o), ro, f"hadamard {B},{Hq},{Hkv},{Nq},{Nk},{d},{causal},{R}")
+    assert np.abs(l.cpu().numpy() - rl).max() < 5e-3
+
+
+def test_prefill_hadamard_outlier_channels(gpu):
+    """The causal GQA workload's outlier-channel K at N=512: rotated parity, and
+    the distance of the plain and the rotated path to unquantized attention
+    (reported)."""
+    from bit_quantized_attention_online_amd import ops
+    from oracle.formats import bf16_bits_to_float64
+    w = dict(synth.WORKLOADS[2], B=1, Nq=512, Nk=512)
+    q = synth.normal_tensor(2, synth.Q_ID, 1, 32, 512, 128)
+    k = np.stack([synth.prefill_k_slice(2, w, 0, h) for h in range(8)])[None]
+    v = synth.normal_tensor(2, synth.V_ID, 1, 8, 512, 128)
+    scale = 1.0 / math.sqrt(128)
+    outs = {}
+    for had in (False, True):
+        outs[had] = from_dev_bf16(ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=True,
+                                                   softmax_scale=scale, v_tile_rows=64, hadamard=had))
+    ro, _ = oatt.qk4v8_prefill_hadamard(q, k, v, scale, True, 64)
+    assert_attn_close(outs[True], ro, "hadamard outlier channels N512")
+    exact, _ = oatt.attention(bf16_bits_to_float64(q), bf16_bits_to_float64(k), bf16_bits_to_float64(v), scale, True)
+    for had in (False, True):
+        rel = np.linalg.norm(outs[had] - exact) / np.linalg.norm(exact)
+        print(f"[report] {'rotated' if had else 'plain'} QK4V8 vs unquantized attention: rel_l2={rel:.3e}", flush=True)
