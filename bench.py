@@ -44,9 +44,15 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def causal_pairs(nq, nk):
+def causal_pairs(nq, nk, window=0):
+    """Visible (query, key) pairs of bottom-right causal attention, optionally
+    limited to the `window` most recent keys of each row."""
     off = nk - nq
-    return sum(min(nk, i + off + 1) for i in range(nq))
+    lim = window if window > 0 else nk
+    return sum(min(lim, i + off + 1) for i in range(nq))
+
+
+SWA_WINDOW = 1024              # the drafter's sliding window (MiMo page, DFlash section)
 
 
 class Events:
@@ -142,8 +148,27 @@ def bench_prefill(torch, ops, synth, steps, warmup):
     torch.cuda.synchronize()
     had = dict(pack_ms=sum(e.ms(0, 1) for e in evh) / steps, attn_ms=sum(e.ms(1, 2) for e in evh) / steps)
     assert torch.isfinite(pph.o.float()).all().item(), "non-finite rotated output"
+    del pph
+    # sliding window of the drafter: the attention kernel on the same packed K/V
+    ppw = ops.PackedPrefill(qd, kd, vd, causal=True, softmax_scale=1.0 / math.sqrt(w["d"]),
+                            v_tile_rows=w["v_tile_rows"], window=SWA_WINDOW)
+    ppw.pack()
+    settle(torch, ppw.attend, seconds=0.2)
+    for _ in range(warmup):
+        ppw.attend()
+    evw = [Events(torch, 2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evw:
+        e.record(0, stream)
+        ppw.attend(stream)
+        e.record(1, stream)
+    torch.cuda.synchronize()
+    swa_ms = sum(e.ms(0, 1) for e in evw) / steps
+    assert torch.isfinite(ppw.o.float()).all().item(), "non-finite windowed output"
+    swa_flops = w["B"] * w["Hq"] * causal_pairs(w["Nq"], w["Nk"], SWA_WINDOW) * 4.0 * w["d"]
+    del ppw
     return dict(w=w, wall_ms=wall * 1e3 / steps, pack_ms=pack_ms, attn_ms=attn_ms, flops=flops, pairs=pairs,
-                fast_ms=fast_ms, had=had)
+                fast_ms=fast_ms, had=had, swa=dict(ms=swa_ms, flops=swa_flops))
 
 
 def build_cache(torch, ops, w, seed):
@@ -178,30 +203,45 @@ def bench_decode(torch, ops, synth, cfg, steps, warmup):
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     ws = torch.empty(max(1, ops.decode_workspace_bytes(q, kc, w["kv_len"], w["v_tile_rows"])), dtype=torch.uint8,
                      device=q.device)
-    run = lambda: ops.attn_decode(q, kc, ks, vc, vs, w["kv_len"], v_tile_rows=w["v_tile_rows"], out=o, workspace=ws,
-                                  softmax_scale=1.0 / math.sqrt(w["d"]))
-    settle(torch, run)
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [Events(torch, 2) for _ in range(steps)]
-    for e in evs:
-        e.record(0, stream)
-        run()
-        e.record(1, stream)
-    torch.cuda.synchronize()
-    ms = sum(e.ms(0, 1) for e in evs) / steps
-    assert torch.isfinite(o.float()).all().item(), "non-finite decode output"
+
+    def timed(window):
+        run = lambda: ops.attn_decode(q, kc, ks, vc, vs, w["kv_len"], v_tile_rows=w["v_tile_rows"], out=o,
+                                      workspace=ws, softmax_scale=1.0 / math.sqrt(w["d"]), window=window)
+        settle(torch, run, seconds=SETTLE_S if window == 0 else 0.2)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        evs = [Events(torch, 2) for _ in range(steps)]
+        for e in evs:
+            e.record(0, stream)
+            run()
+            e.record(1, stream)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all().item(), "non-finite decode output"
+        return sum(e.ms(0, 1) for e in evs) / steps
+
     d = w["d"]
     per_token = d // 2 + d // 32 + d                       # K codes + K scales + V codes per kv-head
-    kv_bytes = w["B"] * w["Hkv"] * (w["kv_len"] * per_token + -(-w["kv_len"] // w["v_tile_rows"]))
     qo_bytes = 2 * (w["B"] * w["q_len"] * w["Hq"] * d * 2)
-    gbs = (kv_bytes + qo_bytes) / (ms * 1e-3) / 1e9
-    out = dict(workload=w["name"], value=round(gbs, 1), unit="GB/s", ms=round(ms, 4),
-               bytes=kv_bytes + qo_bytes,
+
+    def traffic(keys):
+        # the keys' codes and scales plus the V tile scales they span, and Q in / O out
+        return w["B"] * w["Hkv"] * (keys * per_token + -(-keys // w["v_tile_rows"])) + qo_bytes
+
+    ms = timed(0)
+    nbytes = traffic(w["kv_len"])
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = dict(workload=w["name"], value=round(gbs, 1), unit="GB/s", ms=round(ms, 4), bytes=nbytes,
                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                              frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+    # the drafter's sliding window over the same cache: the keys some query of
+    # a sequence can see (window + q_len - 1) are the algorithmic bytes
+    ms_w = timed(SWA_WINDOW)
+    nbytes_w = traffic(min(w["kv_len"], SWA_WINDOW + w["q_len"] - 1))
+    gbs_w = nbytes_w / (ms_w * 1e-3) / 1e9
+    out["sliding_window"] = dict(window=SWA_WINDOW, us=round(ms_w * 1e3, 2), value=round(gbs_w, 1), unit="GB/s",
+                                 bytes=nbytes_w, frac=round(gbs_w / PEAK_HBM_GBS, 4))
     # the cache writer of the same step: q_len new tokens per sequence appended
     # at the end of the cache (the last q_len positions are rewritten)
     out["kv_append"] = bench_append(torch, ops, kc, ks, vc, vs, w["B"], w["Hkv"], d, w["q_len"],
@@ -346,6 +386,12 @@ def main():
                                                           / PEAK_MIXED_TFLOPS, 4),
                               "note": "single-term E4M3 probabilities; about 2e-2 relative L2 from exact attention, "
                                       "outside the 5e-3 gate of the default path"},
+        "prefill_sliding_window": {"window": SWA_WINDOW, "attention_ms": round(pf["swa"]["ms"], 4),
+                                   "algorithmic_flops": pf["swa"]["flops"],
+                                   "value": round(pf["swa"]["flops"] / (pf["swa"]["ms"] * 1e-3) / 1e12, 1),
+                                   "unit": "TFLOP/s",
+                                   "frac_of_mixed_peak": round(pf["swa"]["flops"] / (pf["swa"]["ms"] * 1e-3) / 1e12
+                                                               / PEAK_MIXED_TFLOPS, 4)},
         "prefill_hadamard": {"hadamard": 1, "pack_kv_ms": round(pf["had"]["pack_ms"], 4),
                              "attention_ms": round(pf["had"]["attn_ms"], 4),
                              "value": round(pf["flops"] / ((pf["had"]["pack_ms"] + pf["had"]["attn_ms"]) * 1e-3)

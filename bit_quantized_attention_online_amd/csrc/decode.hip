@@ -15,6 +15,11 @@
 //   gathers 8 keys of one column per lane, which is the P·V A operand layout.
 // Each split writes its normalized fp32 partial output and log2-sum-exp; the
 // merge kernel combines splits with log-sum-exp weights.
+//
+// Sliding window (MiMo page, section "DFlash块扩散推测解码": the drafter keeps
+// only the most recent 1024 keys): the splits cover the keys from the tile
+// holding the first query's first visible key to the end of the sequence, so
+// the work and the traffic do not grow with the length of the cache.
 #include "qk4v8_device.h"
 #include "qk4v8_launch.h"
 
@@ -48,6 +53,7 @@ struct DecodeArgs {
   int64_t n_vtiles_cap;
   float c;          // softmax_scale * log2(e), divided by D for rotated queries
   int hadamard;
+  int window;       // > 0: query t sees only the `window` most recent keys up to its position
 };
 
 template <int D>
@@ -82,7 +88,10 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
   const int64_t bk = blockIdx.x / a.splits;
   const int b = (int)(bk / a.kv_heads), kvh = (int)(bk - (int64_t)b * a.kv_heads);
   const int kvlen = a.kv_lens ? a.kv_lens[b] : a.kv_len;
-  const int j_begin = s * a.tiles_per_split * 128;
+  // first key of the range the splits share: 0, or with a window the start of
+  // the tile holding query 0's first visible key
+  const int j_base = a.window > 0 ? max(0, kvlen - a.q_len + 1 - a.window) & ~127 : 0;
+  const int j_begin = j_base + s * a.tiles_per_split * 128;
   const int j_end = min(kvlen, j_begin + a.tiles_per_split * 128);
   const int ntiles = j_end > j_begin ? (j_end - j_begin + 127) / 128 : 0;
 
@@ -92,6 +101,7 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
   const int qt = row_ok ? mrow / a.group : 0;
   const int head = kvh * a.group + (row_ok ? mrow - qt * a.group : 0);
   const int lim = row_ok ? kvlen - a.q_len + qt : -1;   // last visible key
+  const int low = a.window > 0 ? max(0, lim - a.window + 1) : 0;   // first visible key (clamped at 0)
   uint32_t w[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) w[i] = 0;
@@ -215,14 +225,17 @@ __global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
       const int sa = (int)((reinterpret_cast<const uint32_t*>(lks)[key] >> (8 * klg)) & 0xFF);
       S[t] = mfma16x16x128<kFmtFp4, kFmtFp4>(af, qf, v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc);
     }
-    // ---- mask: keys past this row's limit (covers kv_len and the causal block) ----
-    if (j0 + 127 > kvlen - a.q_len || !row_ok) {
-      // key(t, 4*lg + i) = 16*lg + subtile_key(t, i)
-      const int lim_l = lim - j0 - 16 * lg;
+    // ---- mask: keys past this row's limit (covers kv_len and the causal
+    // block) or, with a window, before its first visible key ----
+    if (j0 + 127 > kvlen - a.q_len || !row_ok || (a.window > 0 && j0 < kvlen - a.window)) {
+      // key(t, 4*lg + i) = j0 + 16*lg + subtile_key(t, i); visible when both
+      // slacks are >= 0, i.e. their OR has no sign bit
+      const int lim_l = lim - j0 - 16 * lg, low_l = low - j0 - 16 * lg;
       static_for<8>([&](auto T) {
         constexpr int t = decltype(T)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[t][i] = mask_score(S[t][i], lim_l - subtile_key(t, i));
+        for (int i = 0; i < 4; ++i)
+          S[t][i] = mask_score(S[t][i], (lim_l - subtile_key(t, i)) | (subtile_key(t, i) - low_l));
       });
     }
     // ---- online softmax + two-term FP8 P ----
@@ -292,8 +305,14 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(const float* __restrict
     lse[((int64_t)b * q_len + qt) * q_heads + head] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
-int decode_num_splits(int batch, int kv_heads, int kv_len, int requested) {
-  const int tiles = (kv_len + 127) / 128;
+int decode_key_span(int kv_len, int q_len, int window) {
+  // with a window the range starts at most 127 keys before query 0's first key
+  if (window > 0 && (int64_t)window + q_len + 126 < kv_len) return window + q_len + 126;
+  return kv_len;
+}
+
+int decode_num_splits(int batch, int kv_heads, int span, int requested) {
+  const int tiles = (span + 127) / 128;
   if (requested > 0) return requested < tiles ? requested : tiles;
   // aim for >= 2048 workgroups in flight, each with >= 4 tiles of work
   const int64_t units = (int64_t)batch * kv_heads;
@@ -316,8 +335,9 @@ static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   DecodeArgs a;
   const int G = p.q_heads / p.kv_heads;
   const int M = G * p.q_len;
-  const int splits = decode_num_splits(p.batch, p.kv_heads, p.kv_len, p.num_splits);
-  const int tiles = (p.kv_len + 127) / 128;
+  const int span = decode_key_span(p.kv_len, p.q_len, p.window);
+  const int splits = decode_num_splits(p.batch, p.kv_heads, span, p.num_splits);
+  const int tiles = (span + 127) / 128;
   a.q = p.q; a.kc = p.k_codes; a.ksc = p.k_scales; a.vc = p.v_codes; a.vsc = p.v_scales; a.kv_lens = p.kv_lens;
   const size_t rows = (size_t)p.batch * p.kv_heads * splits * M;
   a.part_o = reinterpret_cast<float*>(p.ws);
@@ -328,6 +348,7 @@ static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   a.n_vtiles_cap = (p.cap + p.v_tile_rows - 1) / p.v_tile_rows;
   a.c = p.softmax_scale * kLog2e / (p.hadamard ? (float)D : 1.0f);
   a.hadamard = p.hadamard;
+  a.window = p.window < p.kv_len ? p.window : 0;   // a window of kv_len or more keeps every key
   const dim3 grid((unsigned)((int64_t)p.batch * p.kv_heads * splits));
   const int MB = (M + 15) / 16;
   switch (MB) {

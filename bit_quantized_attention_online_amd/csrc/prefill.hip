@@ -294,6 +294,7 @@ struct AttnArgs {
   int64_t n_tiles;
   float c;          // softmax_scale * log2(e), divided by D for rotated Q/K
   int hadamard;     // Q (and the packed K) rotated by H_D
+  int window;       // causal only: > 0 keeps the `window` most recent keys of each row
 };
 
 // Ping-pong schedule.  The 8 waves form two groups of 4 (one wave of each on
@@ -343,18 +344,24 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int p0w = P0 + pb * kRowsPerWave;
   const int off = a.seq_k - a.seq_q;
 
-  // every wave walks the workgroup's tiles; rows that cannot see a tile's
-  // keys are masked
+  // every wave walks the workgroup's tiles t0 .. t0 + nt - 1; rows that
+  // cannot see a tile's keys are masked.  With a sliding window the walk
+  // starts at the tile holding the first key the workgroup's first row sees.
+  const int W = CAUSAL ? a.window : 0;
   const int wg_last_row = min(P0 + a.pos_blocks * kRowsPerWave, a.seq_q) - 1;
   const int kend_wg = CAUSAL ? min(a.seq_k, wg_last_row + off + 1) : a.seq_k;
-  const int nt = (kend_wg + kKvTile - 1) / kKvTile;
+  const int t0 = W > 0 ? max(0, P0 + off - W + 1) / kKvTile : 0;
+  const int nt = (kend_wg + kKvTile - 1) / kKvTile - t0;
   const bool wave_live = p0w < a.seq_q;
   const int mask_lim = CAUSAL ? min(a.seq_k - 1, p0w + off) : a.seq_k - 1;   // tiles past it need the mask
+  // tiles starting before the window's lower edge of the wave's last row need it too
+  const int mask_low = W > 0 ? p0w + kRowsPerWave + off - W : -1;
   const int row = p0w + ql;
   const int row_lim = (CAUSAL ? min(a.seq_k - 1, row + off) : a.seq_k - 1) - 16 * lh;
+  const int row_low = (W > 0 ? max(0, row + off - W + 1) : 0) - 16 * lh;   // first visible key (clamped at 0)
 
   const int64_t bk = (int64_t)b * a.kv_heads + kvh;
-  const uint8_t* const grec = a.rec + bk * a.n_tiles * TB::REC + lane * 16;
+  const uint8_t* const grec = a.rec + (bk * a.n_tiles + t0) * TB::REC + lane * 16;
 
   // ---- Q prologue: this wave's 32 rows to MXFP4 in registers; lane (q, h)
   // holds head_dim block 2s + h of row q for contraction step s ----
@@ -524,15 +531,19 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // VALU step k: mask, online softmax and two-term FP8 split of tile k.
+  // VALU step k: mask, online softmax and two-term FP8 split of tile k
+  // (the workgroup's k-th tile, t0 + k).
   auto valu_step = [&](int k) __attribute__((always_inline)) {
-    if (k * kKvTile + kKvTile - 1 > mask_lim) {      // tiles crossing the diagonal or seq_k
-      // element i of key block kb in this lane is key 32*kb + 16*h + i
-      const int lim = row_lim - k * kKvTile;
+    const int j0 = (t0 + k) * kKvTile;
+    if (j0 + kKvTile - 1 > mask_lim || j0 < mask_low) {   // tiles crossing the diagonal, seq_k or the window edge
+      // element i of key block kb in this lane is key j0 + 32*kb + 16*h + i;
+      // it is visible when both slacks are >= 0, i.e. their OR has no sign bit
+      const int lim = row_lim - j0, low = row_low - j0;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) S[kb][i] = mask_score(S[kb][i], lim - (32 * kb + i));
+        for (int i = 0; i < 16; ++i)
+          S[kb][i] = mask_score(S[kb][i], (lim - (32 * kb + i)) | ((32 * kb + i) - low));
     }
     if constexpr (FAST)
       softmax_tile32_single<NDB>(S, cexp, m_run, O, L, Phi, psc);
@@ -643,6 +654,7 @@ static hipError_t launch_attn_d(const PrefillParams& p, hipStream_t stream) {
   // by D (exact: a power of two)
   a.c = p.softmax_scale * kLog2e / (p.hadamard ? (float)D : 1.0f);
   a.hadamard = p.hadamard;
+  a.window = p.causal && p.window < p.seq_k ? p.window : 0;   // a window of seq_k or more keeps every key
   const int rows_per_wg = a.pos_blocks * kRowsPerWave;
   a.xblocks = p.batch * p.kv_heads * (a.group / a.heads_per_wg);
   a.pos_groups = (p.seq_q + rows_per_wg - 1) / rows_per_wg;

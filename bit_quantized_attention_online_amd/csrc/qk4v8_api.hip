@@ -53,6 +53,7 @@ qk4v8_status validate_prefill(const qk4v8_prefill_args* a) {
   if (a->seq_q > (1 << 30) || a->seq_k > (1 << 30)) return QK4V8_ERR_SHAPE;
   if (a->p_terms != 0 && a->p_terms != 1 && a->p_terms != 2) return QK4V8_ERR_SHAPE;
   if (a->hadamard != 0 && a->hadamard != 1) return QK4V8_ERR_SHAPE;
+  if (a->window < 0 || (a->window > 0 && !a->causal)) return QK4V8_ERR_SHAPE;
   return QK4V8_OK;
 }
 
@@ -86,11 +87,12 @@ qk4v8_status validate_decode(const qk4v8_decode_args* a) {
   if (a->num_splits < 0) return QK4V8_ERR_SHAPE;
   if (!good_scale(a->softmax_scale)) return QK4V8_ERR_SHAPE;
   if (a->hadamard != 0 && a->hadamard != 1) return QK4V8_ERR_SHAPE;
+  if (a->window < 0) return QK4V8_ERR_SHAPE;
   return QK4V8_OK;
 }
 
 int decode_splits(const qk4v8_decode_args* a) {
-  return decode_num_splits(a->batch, a->kv_heads, a->kv_len, a->num_splits);
+  return decode_num_splits(a->batch, a->kv_heads, decode_key_span(a->kv_len, a->q_len, a->window), a->num_splits);
 }
 
 qk4v8_status validate_decode_memory(const qk4v8_decode_args* a) {
@@ -186,6 +188,7 @@ qk4v8_status run_prefill(const qk4v8_prefill_args* a, hipStream_t stream, int pa
   p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows; p.causal = a->causal;
   p.single_term = a->p_terms == 1;
   p.hadamard = a->hadamard;
+  p.window = a->window;
   p.softmax_scale = a->softmax_scale;
   p.ws = static_cast<uint8_t*>(a->workspace);
   if (parts & kPack) {
@@ -268,6 +271,7 @@ qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream) {
   p.cap = a->cap; p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows;
   p.num_splits = a->num_splits; p.softmax_scale = a->softmax_scale;
   p.hadamard = a->hadamard;
+  p.window = a->window;
   p.ws = static_cast<uint8_t*>(a->workspace);
   return from_hip(launch_decode(p, stream));
 }

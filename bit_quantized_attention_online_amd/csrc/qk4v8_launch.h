@@ -35,6 +35,7 @@ struct PrefillParams {
   int batch, q_heads, kv_heads, seq_q, seq_k, head_dim, v_tile_rows, causal;
   int single_term;           // 1: fast mode (one E4M3 term per probability)
   int hadamard;              // 1: Q and K rotated by the Sylvester-Hadamard H_d
+  int window;                // causal sliding window (0: none)
   float softmax_scale;
   uint8_t* ws;
 };
@@ -53,10 +54,13 @@ struct DecodeParams {
   int64_t qs[3], os[3];
   int batch, q_len, q_heads, kv_heads, kv_len, cap, head_dim, v_tile_rows, num_splits;
   int hadamard;              // 1: queries rotated by H_d (the cache K was written rotated)
+  int window;                // sliding window (0: none)
   float softmax_scale;
   uint8_t* ws;
 };
-int decode_num_splits(int batch, int kv_heads, int kv_len, int requested);
+// Keys the split range of one sequence covers at most (kv_len, or less with a window).
+int decode_key_span(int kv_len, int q_len, int window);
+int decode_num_splits(int batch, int kv_heads, int span, int requested);
 size_t decode_workspace_bytes(int batch, int q_len, int q_heads, int kv_heads, int head_dim, int splits);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 

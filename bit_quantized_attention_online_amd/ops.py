@@ -34,7 +34,7 @@ class PrefillArgs(ctypes.Structure):
                 ("v_tile_rows", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("p_terms", ctypes.c_int32), ("hadamard", ctypes.c_int32)]
+                ("p_terms", ctypes.c_int32), ("hadamard", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -47,7 +47,7 @@ class DecodeArgs(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("v_tile_rows", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("hadamard", ctypes.c_int32)]
+                ("hadamard", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 class AppendArgs(ctypes.Structure):
@@ -151,7 +151,7 @@ def quantize_v(v, tile_rows, stream=None):
     return codes, scales
 
 
-def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms=2, hadamard=False):
+def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms=2, hadamard=False, window=0):
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
     a = PrefillArgs()
@@ -166,6 +166,7 @@ def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms=2
     a.softmax_scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
     a.p_terms = p_terms
     a.hadamard = int(bool(hadamard))
+    a.window = window
     return a
 
 
@@ -176,16 +177,17 @@ def prefill_workspace_bytes(q, k, v, causal=False, softmax_scale=None, v_tile_ro
 
 
 def attn_prefill(q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, out=None,
-                 workspace=None, stream=None, p_terms=2, hadamard=False):
+                 workspace=None, stream=None, p_terms=2, hadamard=False, window=0):
     """QK4V8 prefill.  q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d] bf16 (any strides
     with unit innermost).  Returns o [B, Hq, Nq, d] bf16 (and lse fp32
     [B, Hq, Nq] when return_lse).  p_terms=1 selects the single-term fast mode;
-    hadamard=True rotates Q and K by H_d before quantization."""
+    hadamard=True rotates Q and K by H_d before quantization; window=W > 0
+    (causal only) keeps the W most recent keys of each row."""
     for t in (q, k, v):
         _bits16(t)
     o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-    a = _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms, hadamard)
+    a = _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms, hadamard, window)
     need = lib().qk4v8_prefill_workspace_bytes(ctypes.byref(a))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -200,13 +202,13 @@ class PackedPrefill:
     attention kernel from it (used to time the two halves separately)."""
 
     def __init__(self, q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, p_terms=2,
-                 hadamard=False):
+                 hadamard=False, window=0):
         for t in (q, k, v):
             _bits16(t)
         self.o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
         self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
         self.args = _prefill_args(q, k, v, self.o, self.lse, causal, softmax_scale, v_tile_rows, p_terms,
-                                  hadamard)
+                                  hadamard, window)
         need = lib().qk4v8_prefill_workspace_bytes(ctypes.byref(self.args))
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self.args.workspace, self.args.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
@@ -244,16 +246,19 @@ def _decode_args(q, k_codes, k_scales, v_codes, v_scales, o, lse, kv_len, v_tile
     return a
 
 
-def decode_workspace_bytes(q, k_codes, kv_len, v_tile_rows=256, num_splits=0):
+def decode_workspace_bytes(q, k_codes, kv_len, v_tile_rows=256, num_splits=0, window=0):
     a = _decode_args(q, k_codes, k_codes, k_codes, k_codes, q, None, kv_len, v_tile_rows, None, num_splits, None)
+    a.window = window
     return lib().qk4v8_decode_workspace_bytes(ctypes.byref(a))
 
 
 def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256, kv_lens=None, num_splits=0,
-                softmax_scale=None, return_lse=False, out=None, workspace=None, stream=None, hadamard=False):
+                softmax_scale=None, return_lse=False, out=None, workspace=None, stream=None, hadamard=False,
+                window=0):
     """QK4V8 decode / block verify over a quantized cache.
     q [B, q_len, Hq, d] bf16; k_codes [B, Hkv, cap, d/2], k_scales [B, Hkv, cap, d/32],
     v_codes [B, Hkv, cap, d], v_scales [B, Hkv, ceil(cap/v_tile_rows)] uint8.
+    window=W > 0 keeps the W most recent keys of each query.
     Returns o [B, q_len, Hq, d] bf16 (and lse fp32 [B, q_len, Hq])."""
     _bits16(q)
     o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -263,6 +268,7 @@ def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256
     a = _decode_args(q, k_codes, k_scales, v_codes, v_scales, o, lse, kv_len, v_tile_rows, kv_lens, num_splits,
                      softmax_scale)
     a.hadamard = int(bool(hadamard))
+    a.window = window
     need = lib().qk4v8_decode_workspace_bytes(ctypes.byref(a))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QK4V8_ABI_VERSION 4
+#define QK4V8_ABI_VERSION 5
 
 typedef enum {
   QK4V8_OK = 0,
@@ -149,6 +149,12 @@ qk4v8_status qk4v8_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int3
  *               the scores are multiplied by softmax_scale / d, since
  *               (H q).(H k) = d (q.k): exact attention is unchanged and only
  *               the quantization error moves.  0: no rotation.
+ *   window    : causal sliding window (MiMo page, section "DFlash块扩散推测解码":
+ *               the drafter attends to the most recent 1024 keys only).  0: no
+ *               window; W > 0 (needs causal = 1): row i sees keys j with
+ *               i + seq_k - seq_q - W < j <= i + seq_k - seq_q, and the call
+ *               reads only the key tiles some row of a workgroup can see.
+ *               W >= seq_k is the same as 0.
  */
 typedef struct {
   const uint16_t* q;
@@ -166,6 +172,7 @@ typedef struct {
   size_t workspace_bytes;
   int32_t p_terms;
   int32_t hadamard;
+  int32_t window;
 } qk4v8_prefill_args;
 
 /* Workspace bytes qk4v8_attn_prefill needs for these sizes (0 on bad sizes). */
@@ -214,6 +221,11 @@ qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t 
  *               (qk4v8_kv_append with hadamard = 1); the queries are then
  *               rotated the same way and the scores multiplied by
  *               softmax_scale / head_dim (see qk4v8_prefill_args).  0: neither.
+ *   window    : sliding window W (see qk4v8_prefill_args); 0: none.  Query t
+ *               sees keys j with kv_len_b - q_len + t - W < j <= kv_len_b -
+ *               q_len + t; the splits cover only the keys from the 128-key tile
+ *               holding query 0's first visible key, so the traffic and the
+ *               workspace are bounded by W + q_len + 126 keys per sequence.
  */
 typedef struct {
   const uint16_t* q;
@@ -231,6 +243,7 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   int32_t hadamard;
+  int32_t window;
 } qk4v8_decode_args;
 
 /* Workspace bytes qk4v8_attn_decode needs for these sizes (0 on bad sizes). */

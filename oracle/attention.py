@@ -14,6 +14,10 @@ rounding of the probabilities:
     lse_i = max_j s_ij + ln(sum_j p_ij)     (natural log)
 
 GQA: query head h reads KV head floor(h / G), G = Hq / Hkv.
+Sliding window (MiMo page, section "DFlash块扩散推测解码": the drafter attends
+only to the most recent 1024 tokens): with a window W > 0, row i additionally
+drops keys j <= i + (Nk - Nq) - W, i.e. it sees at most the W most recent keys
+up to and including its own position.
 Decode / block verify (MiMo page, section "DFlash块扩散推测解码": the backbone
 checks a drafted block of q_len tokens in one pass) is the same definition with
 Nq = q_len queries placed at the end of an Nk-long sequence, i.e. the causal
@@ -28,12 +32,16 @@ from .quant import dequantize_qk, dequantize_v, quantize_qk, quantize_qk_hadamar
 _CHUNK_ELEMS = 1 << 25
 
 
-def _rows_attention(q, k, v, sigma, limits):
-    """q [R, d], k/v [Nk, d] float64; limits[r] = last visible key index of
-    row r (or Nk-1 when not causal).  Returns (o [R, d], lse [R])."""
+def _visible(cols, limits, lows):
+    return (cols[None, :] <= limits[:, None]) & (cols[None, :] >= lows[:, None])
+
+
+def _rows_attention(q, k, v, sigma, limits, lows):
+    """q [R, d], k/v [Nk, d] float64; row r sees keys lows[r] <= j <= limits[r].
+    Returns (o [R, d], lse [R])."""
     s = sigma * (q @ k.T)
     cols = np.arange(k.shape[0])
-    s = np.where(cols[None, :] <= limits[:, None], s, -np.inf)
+    s = np.where(_visible(cols, limits, lows), s, -np.inf)
     m = s.max(axis=1)
     p = np.exp(s - m[:, None])
     l = p.sum(axis=1)
@@ -41,8 +49,14 @@ def _rows_attention(q, k, v, sigma, limits):
     return o, m + np.log(l)
 
 
-def attention(q, k, v, softmax_scale, causal, rows=None):
-    """Exact float64 attention.
+def _limits(pos, Nq, Nk, causal, window):
+    limits = pos + (Nk - Nq) if causal else np.full(len(pos), Nk - 1)
+    lows = limits - window + 1 if window else np.zeros(len(pos), dtype=np.int64)
+    return limits, lows
+
+
+def attention(q, k, v, softmax_scale, causal, rows=None, window=0):
+    """Exact float64 attention (``window`` > 0: sliding window, causal only).
 
     q: [B, Hq, Nq, d]  (or [B, Hq, R, d] when ``rows`` selects R query
        positions out of Nq = rows_total, see below)
@@ -63,7 +77,8 @@ def attention(q, k, v, softmax_scale, causal, rows=None):
     else:
         pos, Nq = np.asarray(rows[0]), rows[1]
     sigma = float(np.float32(softmax_scale))
-    limits = pos + (Nk - Nq) if causal else np.full(R, Nk - 1)
+    assert not window or causal
+    limits, lows = _limits(pos, Nq, Nk, causal, window)
     o = np.zeros((B, Hq, R, d))
     lse = np.zeros((B, Hq, R))
     step = max(1, _CHUNK_ELEMS // max(Nk, 1))
@@ -72,7 +87,8 @@ def attention(q, k, v, softmax_scale, causal, rows=None):
             g = h // G
             for r0 in range(0, R, step):
                 sl = slice(r0, min(R, r0 + step))
-                o[b, h, sl], lse[b, h, sl] = _rows_attention(q[b, h, sl], k[b, g], v[b, g], sigma, limits[sl])
+                o[b, h, sl], lse[b, h, sl] = _rows_attention(q[b, h, sl], k[b, g], v[b, g], sigma, limits[sl],
+                                                             lows[sl])
     return o, lse
 
 
@@ -96,7 +112,7 @@ def probabilities(q, k, softmax_scale, causal):
     return out
 
 
-def qk4v8_prefill(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_rows, rows=None):
+def qk4v8_prefill(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_rows, rows=None, window=0):
     """The whole QK4V8 prefill on the CPU: MXFP4 Q and K, per-tile FP8 V,
     then exact attention of the dequantized operands.
 
@@ -109,10 +125,10 @@ def qk4v8_prefill(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_rows, ro
     B, Hkv, Nk, d = v_bits.shape
     vc, vs = quantize_v(v_bits.reshape(B * Hkv, Nk, d), v_tile_rows)
     vh = dequantize_v(vc, vs, v_tile_rows).reshape(B, Hkv, Nk, d)
-    return attention(qh, kh, vh, softmax_scale, causal, rows=rows)
+    return attention(qh, kh, vh, softmax_scale, causal, rows=rows, window=window)
 
 
-def qk4v8_decode(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens, v_tile_rows, softmax_scale):
+def qk4v8_decode(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens, v_tile_rows, softmax_scale, window=0):
     """QK4V8 decode / block verify over a quantized cache.
 
     q_bits: uint16 [B, q_len, Hq, d]; caches: k_codes [B, Hkv, cap, d/2],
@@ -130,7 +146,7 @@ def qk4v8_decode(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens, v_tile_r
         n = int(kv_lens[b])
         kh = dequantize_qk(k_codes[b, :, :n], k_scales[b, :, :n])
         vh = dequantize_v(v_codes[b, :, :n], v_scales[b], v_tile_rows)
-        ob, lb = attention(qh[b:b + 1], kh[None], vh[None], softmax_scale, causal=True)
+        ob, lb = attention(qh[b:b + 1], kh[None], vh[None], softmax_scale, causal=True, window=window)
         o[b] = ob[0].transpose(1, 0, 2)
         lse[b] = lb[0].T
     return o, lse
@@ -156,11 +172,11 @@ FAST_P_HEADROOM = 7
 _LOG2E = 1.4426950408889634
 
 
-def _rows_attention_fast(q, k, v, sigma, limits):
+def _rows_attention_fast(q, k, v, sigma, limits, lows):
     s = sigma * (q @ k.T)
     Nk = k.shape[0]
     cols = np.arange(Nk)
-    t = np.where(cols[None, :] <= limits[:, None], s * _LOG2E, -np.inf)
+    t = np.where(_visible(cols, limits, lows), s * _LOG2E, -np.inf)
     M = np.floor(t.max(axis=1))                                  # common integer shift per row
     t = t - M[:, None]
     nb = -(-Nk // FAST_P_BLOCK)
@@ -177,7 +193,7 @@ def _rows_attention_fast(q, k, v, sigma, limits):
     return o, (M + np.log2(l)) * np.log(2.0)
 
 
-def attention_fast_p(q, k, v, softmax_scale, causal, rows=None):
+def attention_fast_p(q, k, v, softmax_scale, causal, rows=None, window=0):
     """Attention with single-term E4M3 probabilities (definition above);
     same arguments and returns as ``attention``."""
     q = np.asarray(q, dtype=np.float64)
@@ -191,7 +207,8 @@ def attention_fast_p(q, k, v, softmax_scale, causal, rows=None):
     else:
         pos, Nq = np.asarray(rows[0]), rows[1]
     sigma = float(np.float32(softmax_scale))
-    limits = pos + (Nk - Nq) if causal else np.full(R, Nk - 1)
+    assert not window or causal
+    limits, lows = _limits(pos, Nq, Nk, causal, window)
     o = np.zeros((B, Hq, R, d))
     lse = np.zeros((B, Hq, R))
     step = max(1, _CHUNK_ELEMS // max(Nk, 1))
@@ -200,18 +217,18 @@ def attention_fast_p(q, k, v, softmax_scale, causal, rows=None):
             for r0 in range(0, R, step):
                 sl = slice(r0, min(R, r0 + step))
                 o[b, h, sl], lse[b, h, sl] = _rows_attention_fast(q[b, h, sl], k[b, h // G], v[b, h // G], sigma,
-                                                                  limits[sl])
+                                                                  limits[sl], lows[sl])
     return o, lse
 
 
-def qk4v8_prefill_fast(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_rows, rows=None):
+def qk4v8_prefill_fast(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_rows, rows=None, window=0):
     """``qk4v8_prefill`` with single-term FP8 probabilities."""
     qh = dequantize_qk(*quantize_qk(q_bits))
     kh = dequantize_qk(*quantize_qk(k_bits))
     B, Hkv, Nk, d = v_bits.shape
     vc, vs = quantize_v(v_bits.reshape(B * Hkv, Nk, d), v_tile_rows)
     vh = dequantize_v(vc, vs, v_tile_rows).reshape(B, Hkv, Nk, d)
-    return attention_fast_p(qh, kh, vh, softmax_scale, causal, rows=rows)
+    return attention_fast_p(qh, kh, vh, softmax_scale, causal, rows=rows, window=window)
 
 
 # ---------------------------------------------------------------------------
@@ -221,7 +238,7 @@ def qk4v8_prefill_fast(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_row
 # (exact: d is a power of two).  V is unchanged.
 # ---------------------------------------------------------------------------
 
-def qk4v8_prefill_hadamard(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_rows, rows=None):
+def qk4v8_prefill_hadamard(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile_rows, rows=None, window=0):
     """``qk4v8_prefill`` with rotated Q and K."""
     d = q_bits.shape[-1]
     qh = dequantize_qk(*quantize_qk_hadamard(q_bits))
@@ -229,10 +246,11 @@ def qk4v8_prefill_hadamard(q_bits, k_bits, v_bits, softmax_scale, causal, v_tile
     B, Hkv, Nk, _ = v_bits.shape
     vc, vs = quantize_v(v_bits.reshape(B * Hkv, Nk, d), v_tile_rows)
     vh = dequantize_v(vc, vs, v_tile_rows).reshape(B, Hkv, Nk, d)
-    return attention(qh, kh, vh, float(np.float32(softmax_scale)) / d, causal, rows=rows)
+    return attention(qh, kh, vh, float(np.float32(softmax_scale)) / d, causal, rows=rows, window=window)
 
 
-def qk4v8_decode_hadamard(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens, v_tile_rows, softmax_scale):
+def qk4v8_decode_hadamard(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens, v_tile_rows, softmax_scale,
+                          window=0):
     """``qk4v8_decode`` over a cache whose K rows were rotated before
     quantization; the queries are rotated the same way."""
     B, q_len, Hq, d = q_bits.shape
@@ -243,7 +261,8 @@ def qk4v8_decode_hadamard(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens,
         n = int(kv_lens[b])
         kh = dequantize_qk(k_codes[b, :, :n], k_scales[b, :, :n])
         vh = dequantize_v(v_codes[b, :, :n], v_scales[b], v_tile_rows)
-        ob, lb = attention(qh[b:b + 1], kh[None], vh[None], float(np.float32(softmax_scale)) / d, causal=True)
+        ob, lb = attention(qh[b:b + 1], kh[None], vh[None], float(np.float32(softmax_scale)) / d, causal=True,
+                           window=window)
         o[b] = ob[0].transpose(1, 0, 2)
         lse[b] = lb[0].T
     return o, lse

@@ -143,3 +143,21 @@ def hadamard_row_f32(values):
                 x[i], x[i + h] = _f32(a + b), _f32(a - b)
         h *= 2
     return x
+
+
+def attention_rows_window(q, k, v, sigma, window):
+    """Bottom-right causal attention where row i sees only the ``window`` most
+    recent keys up to its position, by loops (second route for the window
+    mask)."""
+    nq, nk = len(q), len(k)
+    out, lses = [], []
+    for i in range(nq):
+        last = i + (nk - nq)
+        first = max(0, last - window + 1)
+        s = [sigma * math.fsum(a * b for a, b in zip(q[i], k[j])) for j in range(first, last + 1)]
+        m = max(s)
+        p = [math.exp(x - m) for x in s]
+        l = math.fsum(p)
+        out.append([math.fsum(p[j] * v[first + j][c] for j in range(len(p))) / l for c in range(len(v[0]))])
+        lses.append(m + math.log(l))
+    return out, lses

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.qk4v8_abi_version() == 4
+    assert L.qk4v8_abi_version() == 5
     for s in range(7):
         assert L.qk4v8_status_string(s)
 
@@ -67,7 +67,7 @@ def _prefill(**kw):
     (dict(causal=2), 2), (dict(seq_q=65), 2), (dict(softmax_scale=0.0), 2), (dict(softmax_scale=float("nan")), 2),
     (dict(q=None), 1), (dict(q_stride=[64 * 128, 128, 36]), 3), (dict(o_stride=[64 * 128, 128, 4]), 3),
     (dict(k=4100), 3), (dict(workspace=None), 5), (dict(workspace=1 << 20 | 8), 5), (dict(workspace_bytes=16), 5),
-    (dict(p_terms=3), 2), (dict(hadamard=2), 2),
+    (dict(p_terms=3), 2), (dict(hadamard=2), 2), (dict(window=-1), 2), (dict(window=16, causal=0), 2),
 ])
 def test_prefill_validation(kw, status):
     a = _prefill(**kw)
@@ -105,6 +105,7 @@ def _decode(**kw):
     (dict(q_len=9), 2), (dict(kv_len=1025), 2), (dict(kv_len=0), 2), (dict(head_dim=256), 2),
     (dict(v_tile_rows=16), 2), (dict(num_splits=-1), 2), (dict(v_codes=None), 1),
     (dict(q_stride=[64 * 128, 64 * 128, 100]), 3), (dict(k_codes=4104), 3), (dict(workspace_bytes=0), 5),
+    (dict(window=-3), 2),
 ])
 def test_decode_validation(kw, status):
     assert ops.lib().qk4v8_attn_decode(ctypes.byref(_decode(**kw)), None) == status
@@ -117,6 +118,20 @@ def test_decode_workspace_query():
     rows = 2 * 8 * 4 * 8
     assert L.qk4v8_decode_workspace_bytes(ctypes.byref(a)) >= rows * (128 * 4 + 4)
     assert L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(q_len=9))) == 0
+
+
+def test_decode_window_bounds_the_splits():
+    # with a window the splits cover at most window + q_len + 126 keys, so the
+    # library's own split count (and workspace) stops growing with kv_len
+    L = ops.lib()
+    big = dict(batch=1, kv_heads=1, kv_len=1 << 20, cap=1 << 20)
+    full = L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(**big)))
+    win = L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(window=1024, **big)))
+    win2 = L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(window=1024, **dict(big, kv_len=1 << 19))))
+    assert win < full and win == win2
+    # a window that covers every key is no window
+    assert L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(window=1000))) == \
+        L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode()))
 
 
 def _append(**kw):

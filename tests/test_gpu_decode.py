@@ -130,6 +130,16 @@ def test_decode_workloads_full_size_sampled(gpu, cfg):
         ro, _ = oatt.qk4v8_decode(q[b:b + 1], rkc[None], rks[None], rvc[None], rvs[None],
                                   np.array([w["kv_len"]]), w["v_tile_rows"], 1 / math.sqrt(w["d"]))
         assert_attn_close(o[b:b + 1], ro, f"workload {cfg} batch {b}")
+    # the same cache with the drafter's 1024-key sliding window
+    ow = from_dev_bf16(ops.attn_decode(to_dev(q), kc, ks, vc, vs, w["kv_len"], v_tile_rows=w["v_tile_rows"],
+                                       window=1024))
+    for b in sample_b:
+        kb, vb = kept[b]
+        rkc, rks = quant.quantize_qk(kb)
+        rvc, rvs = quant.quantize_v(vb, w["v_tile_rows"])
+        ro, _ = oatt.qk4v8_decode(q[b:b + 1], rkc[None], rks[None], rvc[None], rvs[None],
+                                  np.array([w["kv_len"]]), w["v_tile_rows"], 1 / math.sqrt(w["d"]), window=1024)
+        assert_attn_close(ow[b:b + 1], ro, f"workload {cfg} window 1024 batch {b}")
 
 
 @pytest.mark.parametrize("q_len,d", [(1, 128), (4, 128), (2, 64)])
