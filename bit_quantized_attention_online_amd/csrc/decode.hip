@@ -72,8 +72,17 @@ __device__ __forceinline__ int vswz(int row, int chunk) {
   return chunk ^ (row & (DecTile<D>::NC - 1));
 }
 
+// Resident workgroups per CU (4 SIMDs x waves per SIMD / MB), from the
+// kernels' register use: at head_dim 128 one wave per SIMD for MB = 1, 2
+// (the next tile is staged in registers), two for MB = 3 and three for MB = 4
+// (register budget 168); at head_dim 64 two for MB <= 3 and three for MB = 4.
+__host__ __device__ constexpr int decode_wgs_per_cu(int D, int MB) {
+  return MB == 4 ? 3 : (D == 128 ? (MB == 3 ? 8 : 4) : 8) / MB;
+}
+
 template <int D, int MB>
-__global__ void __launch_bounds__(MB * 64) decode_split_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(MB * 64) __attribute__((amdgpu_waves_per_eu(MB == 4 ? 3 : 1, 8)))
+decode_split_kernel(DecodeArgs a) {
   using T = DecTile<D>;
   constexpr int NB = T::NB, NC = T::NC, ND = D / 16;
   constexpr int NT = MB * 64;
@@ -311,12 +320,16 @@ int decode_key_span(int kv_len, int q_len, int window) {
   return kv_len;
 }
 
-int decode_num_splits(int batch, int kv_heads, int span, int requested) {
+int decode_num_splits(int batch, int kv_heads, int rows, int head_dim, int span, int requested) {
   const int tiles = (span + 127) / 128;
   if (requested > 0) return requested < tiles ? requested : tiles;
-  // aim for >= 2048 workgroups in flight, each with >= 4 tiles of work
+  // one round of workgroups: as many as the 256 CUs hold at once (a second,
+  // partial round and larger split partials cost more than they balance),
+  // each with >= 4 tiles of work
+  const int MB = rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 48 ? 3 : 4;
   const int64_t units = (int64_t)batch * kv_heads;
-  int s = (int)((2048 + units - 1) / units);
+  const int64_t capacity = 256 * (int64_t)decode_wgs_per_cu(head_dim, MB);
+  int s = (int)((capacity + units / 2) / units);
   const int max_s = tiles / 4 > 0 ? tiles / 4 : 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
@@ -336,7 +349,7 @@ static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   const int G = p.q_heads / p.kv_heads;
   const int M = G * p.q_len;
   const int span = decode_key_span(p.kv_len, p.q_len, p.window);
-  const int splits = decode_num_splits(p.batch, p.kv_heads, span, p.num_splits);
+  const int splits = decode_num_splits(p.batch, p.kv_heads, M, D, span, p.num_splits);
   const int tiles = (span + 127) / 128;
   a.q = p.q; a.kc = p.k_codes; a.ksc = p.k_scales; a.vc = p.v_codes; a.vsc = p.v_scales; a.kv_lens = p.kv_lens;
   const size_t rows = (size_t)p.batch * p.kv_heads * splits * M;

@@ -92,7 +92,8 @@ qk4v8_status validate_decode(const qk4v8_decode_args* a) {
 }
 
 int decode_splits(const qk4v8_decode_args* a) {
-  return decode_num_splits(a->batch, a->kv_heads, decode_key_span(a->kv_len, a->q_len, a->window), a->num_splits);
+  return decode_num_splits(a->batch, a->kv_heads, (a->q_heads / a->kv_heads) * a->q_len, a->head_dim,
+                           decode_key_span(a->kv_len, a->q_len, a->window), a->num_splits);
 }
 
 qk4v8_status validate_decode_memory(const qk4v8_decode_args* a) {

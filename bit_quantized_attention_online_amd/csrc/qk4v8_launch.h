@@ -60,7 +60,8 @@ struct DecodeParams {
 };
 // Keys the split range of one sequence covers at most (kv_len, or less with a window).
 int decode_key_span(int kv_len, int q_len, int window);
-int decode_num_splits(int batch, int kv_heads, int span, int requested);
+// Splits of the KV range per (batch, kv-head); rows = (q_heads / kv_heads) * q_len.
+int decode_num_splits(int batch, int kv_heads, int rows, int head_dim, int span, int requested);
 size_t decode_workspace_bytes(int batch, int q_len, int q_heads, int kv_heads, int head_dim, int splits);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
