@@ -110,7 +110,9 @@ decode_split_kernel(DecodeArgs a) {
   const int qt = row_ok ? mrow / a.group : 0;
   const int head = kvh * a.group + (row_ok ? mrow - qt * a.group : 0);
   const int lim = row_ok ? kvlen - a.q_len + qt : -1;   // last visible key
-  const int low = a.window > 0 ? max(0, lim - a.window + 1) : 0;   // first visible key (clamped at 0)
+  // first visible key (clamped at 0) and the count after it; rows past M see nothing
+  const int low = !row_ok ? (1 << 30) : a.window > 0 ? max(0, lim - a.window + 1) : 0;
+  const uint32_t span = row_ok ? (uint32_t)(lim - low) : 0u;
   uint32_t w[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) w[i] = 0;
@@ -237,14 +239,12 @@ decode_split_kernel(DecodeArgs a) {
     // ---- mask: keys past this row's limit (covers kv_len and the causal
     // block) or, with a window, before its first visible key ----
     if (j0 + 127 > kvlen - a.q_len || !row_ok || (a.window > 0 && j0 < kvlen - a.window)) {
-      // key(t, 4*lg + i) = j0 + 16*lg + subtile_key(t, i); visible when both
-      // slacks are >= 0, i.e. their OR has no sign bit
-      const int lim_l = lim - j0 - 16 * lg, low_l = low - j0 - 16 * lg;
+      // key(t, 4*lg + i) = j0 + 16*lg + subtile_key(t, i)
+      const int low_l = low - j0 - 16 * lg;
       static_for<8>([&](auto T) {
         constexpr int t = decltype(T)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          S[t][i] = mask_score(S[t][i], (lim_l - subtile_key(t, i)) | (subtile_key(t, i) - low_l));
+        for (int i = 0; i < 4; ++i) S[t][i] = mask_range(S[t][i], subtile_key(t, i), low_l, span);
       });
     }
     // ---- online softmax + two-term FP8 P ----

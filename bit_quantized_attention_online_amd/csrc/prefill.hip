@@ -359,6 +359,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int row = p0w + ql;
   const int row_lim = (CAUSAL ? min(a.seq_k - 1, row + off) : a.seq_k - 1) - 16 * lh;
   const int row_low = (W > 0 ? max(0, row + off - W + 1) : 0) - 16 * lh;   // first visible key (clamped at 0)
+  // visible keys row_low .. row_low + row_span (rows past seq_q are never stored)
+  const uint32_t row_span = (uint32_t)max(row_lim - row_low, 0);
 
   const int64_t bk = (int64_t)b * a.kv_heads + kvh;
   const uint8_t* const grec = a.rec + (bk * a.n_tiles + t0) * TB::REC + lane * 16;
@@ -536,14 +538,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto valu_step = [&](int k) __attribute__((always_inline)) {
     const int j0 = (t0 + k) * kKvTile;
     if (j0 + kKvTile - 1 > mask_lim || j0 < mask_low) {   // tiles crossing the diagonal, seq_k or the window edge
-      // element i of key block kb in this lane is key j0 + 32*kb + 16*h + i;
-      // it is visible when both slacks are >= 0, i.e. their OR has no sign bit
-      const int lim = row_lim - j0, low = row_low - j0;
+      // element i of key block kb in this lane is key j0 + 32*kb + 16*h + i
+      const int low = row_low - j0;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          S[kb][i] = mask_score(S[kb][i], (lim - (32 * kb + i)) | ((32 * kb + i) - low));
+        for (int i = 0; i < 16; ++i) S[kb][i] = mask_range(S[kb][i], 32 * kb + i, low, row_span);
     }
     if constexpr (FAST)
       softmax_tile32_single<NDB>(S, cexp, m_run, O, L, Phi, psc);

@@ -207,11 +207,11 @@ __device__ __forceinline__ uint32_t e4m3_put2(uint32_t old, float a, float b, fl
   return __builtin_bit_cast(uint32_t, o);
 }
 
-// Causal / length mask without compare masks: slack >= 0 keeps the score,
-// slack < 0 turns it into -inf (min with +inf or -inf built from the sign bit).
-__device__ __forceinline__ float mask_score(float s, int slack) {
-  const float bound = __uint_as_float(((uint32_t)slack & 0x80000000u) | 0x7F800000u);
-  return fminf(s, bound);
+// Causal / window / length mask: the score of the key at offset x survives
+// when low <= x <= low + span, one unsigned range compare (x - low wraps to
+// a huge value below low); masked scores become -inf.
+__device__ __forceinline__ float mask_range(float s, int x, int low, uint32_t span) {
+  return (uint32_t)(x - low) <= span ? s : -INFINITY;
 }
 
 constexpr float kLazyRescale = 8.0f;   // log2 headroom before the accumulator is rescaled
