@@ -48,6 +48,11 @@ struct DecodeArgs {
   const int32_t* kv_lens;
   float* part_o;      // [bk][split][M][D]
   float* part_lse;    // [bk][split][M]  (log2 domain)
+  uint16_t* o;        // final output and lse, written directly by a single split
+  float* lse;
+  int64_t os0, os1, os2;
+  int q_heads;
+  int direct;         // one split and an 8-byte aligned output: no merge pass
   int64_t qs0, qs1, qs2;
   int kv_heads, group, q_len, M, kv_len, cap, R, splits, tiles_per_split;
   int64_t n_vtiles_cap;
@@ -272,12 +277,25 @@ decode_split_kernel(DecodeArgs a) {
     L = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Plo, L, 127, psc - 4);
   }
 
-  // ---- write this split's normalized partial and its log2-sum-exp ----
+  // ---- write this split's normalized partial and its log2-sum-exp (one
+  // split: the final bf16 output and natural-log lse, as the merge would) ----
   if (!row_ok) return;
   const float l = L[0];
   const int64_t prow = (bk * a.splits + s) * a.M + mrow;
   const bool empty = !(l > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l;
+  if (a.direct) {
+    uint16_t* orow = a.o + b * a.os0 + qt * a.os1 + (int64_t)head * a.os2;
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) {
+      const v4f v = O[dd] * inv;
+      *reinterpret_cast<uint2*>(orow + dd * 16 + 4 * lg) =
+          make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+    }
+    if (a.lse != nullptr && lg == 0)
+      a.lse[((int64_t)b * a.q_len + qt) * a.q_heads + head] = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
+    return;
+  }
   float* dst = a.part_o + prow * D;
 #pragma unroll
   for (int dd = 0; dd < ND; ++dd) *reinterpret_cast<v4f*>(dst + dd * 16 + 4 * lg) = O[dd] * inv;
@@ -325,12 +343,13 @@ int decode_num_splits(int batch, int kv_heads, int rows, int head_dim, int span,
   if (requested > 0) return requested < tiles ? requested : tiles;
   // one round of workgroups: as many as the 256 CUs hold at once (a second,
   // partial round and larger split partials cost more than they balance),
-  // each with >= 4 tiles of work
+  // each with >= 8 tiles of work (below that the merge pass costs more than
+  // the parallelism gains; one split writes the output without it)
   const int MB = rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 48 ? 3 : 4;
   const int64_t units = (int64_t)batch * kv_heads;
   const int64_t capacity = 256 * (int64_t)decode_wgs_per_cu(head_dim, MB);
   int s = (int)((capacity + units / 2) / units);
-  const int max_s = tiles / 4 > 0 ? tiles / 4 : 1;
+  const int max_s = tiles / 8 > 0 ? tiles / 8 : 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   return s;
@@ -362,6 +381,9 @@ static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   a.c = p.softmax_scale * kLog2e / (p.hadamard ? (float)D : 1.0f);
   a.hadamard = p.hadamard;
   a.window = p.window < p.kv_len ? p.window : 0;   // a window of kv_len or more keeps every key
+  a.o = p.o; a.lse = p.lse; a.os0 = p.os[0]; a.os1 = p.os[1]; a.os2 = p.os[2]; a.q_heads = p.q_heads;
+  a.direct = splits == 1 && (reinterpret_cast<uintptr_t>(p.o) & 7) == 0 && p.os[0] % 4 == 0 && p.os[1] % 4 == 0 &&
+             p.os[2] % 4 == 0;
   const dim3 grid((unsigned)((int64_t)p.batch * p.kv_heads * splits));
   const int MB = (M + 15) / 16;
   switch (MB) {
@@ -371,7 +393,7 @@ static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
     default: hipLaunchKernelGGL((decode_split_kernel<D, 4>), grid, dim3(256), 0, stream, a); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.direct) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((int64_t)p.batch * p.kv_heads * M)), dim3(D), 0,
                      stream, a.part_o, a.part_lse, p.kv_heads, G, M, splits, p.o, p.os[0], p.os[1], p.os[2], p.lse,
                      p.q_heads, p.q_len);

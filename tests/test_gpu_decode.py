@@ -173,3 +173,30 @@ def test_decode_hadamard(gpu, q_len, d):
     ro, rl = oatt.qk4v8_decode_hadamard(q, rk, rks, rv, rvs, np.array([n] * B), R, 1 / math.sqrt(d))
     assert_attn_close(from_dev_bf16(o), ro, f"decode hadamard q_len{q_len} d{d}")
     assert np.abs(l.cpu().numpy() - rl).max() < 5e-3
+
+
+def test_decode_single_split_direct_and_merged_agree(gpu):
+    """With one split the kernel writes the final output itself when the
+    output is 8-byte aligned with strides in multiples of 4 elements;
+    otherwise the merge pass writes it.  Both must give the same bits."""
+    from bit_quantized_attention_online_amd import ops
+    B, Hq, Hkv, d, q_len, n, R = 2, 8, 2, 128, 2, 900, 256
+    rng = np.random.default_rng(17)
+    k = synth.bf16_bits(rng.standard_normal((B, Hkv, n, d)).astype(np.float32))
+    v = synth.bf16_bits(rng.standard_normal((B, Hkv, n, d)).astype(np.float32))
+    q = synth.bf16_bits(rng.standard_normal((B, q_len, Hq, d)).astype(np.float32))
+    kc, ks, vc, vs = _cache_from(k, v, R)
+    qd = to_dev(q)
+    print("[case] decode one split, direct and merged output", flush=True)
+    o1, l1 = ops.attn_decode(qd, kc, ks, vc, vs, n, v_tile_rows=R, num_splits=1, return_lse=True)
+    wide = torch.zeros((B, q_len, Hq, d + 2), dtype=torch.bfloat16, device=qd.device)
+    o2, l2 = ops.attn_decode(qd, kc, ks, vc, vs, n, v_tile_rows=R, num_splits=1, return_lse=True,
+                             out=wide[..., :d])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.count_nonzero(wide[..., d:]) == 0
+    rkc, rks = quant.quantize_qk(k)
+    rvc, rvs = quant.quantize_v(v.reshape(B * Hkv, n, d), R)
+    ro, _ = oatt.qk4v8_decode(q, rkc, rks, rvc.reshape(B, Hkv, n, d), rvs.reshape(B, Hkv, -1), np.array([n] * B), R,
+                              1 / math.sqrt(d))
+    assert_attn_close(from_dev_bf16(o1), ro, "decode one split")
