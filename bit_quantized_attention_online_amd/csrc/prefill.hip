@@ -221,30 +221,72 @@ __global__ void __launch_bounds__(256) vtile_scale_kernel(const uint16_t* __rest
 //           (column d = 32*db + m, keys 64*s2 + 32*half + 16*h .. +15)
 //   scales: u32, byte b = E8M0 of the V tile holding key 32b    at K + VS_OFF
 // ---------------------------------------------------------------------------
-template <int D>
+// FUSED (V tiles of R <= 128 rows, which never straddle a 128-key tile): the
+// workgroup computes the scales of its own V tiles from the rows it holds in
+// registers instead of reading them from the vtile_scale pre-pass.
+template <int D, bool FUSED>
 __global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict__ v, int64_t vs0, int64_t vs1,
                                                      int64_t vs2, int kv_heads, int seq_k, int R, int64_t n_tiles,
                                                      int64_t n_vtiles, const uint8_t* __restrict__ vtile,
                                                      uint8_t* __restrict__ rec) {
   using TB = TileBytes<D>;
   constexpr int LDSROW = D + 4;   // bytes per key row in LDS (padding spreads banks)
+  constexpr int CPR = D / 8;
+  constexpr int PER = kKvTile * CPR / 256;   // 16-byte chunks per thread (rows tid/CPR + (256/CPR)*i)
   __shared__ uint8_t tileb[kKvTile * LDSROW];
+  __shared__ float red[4][4];
+  __shared__ uint8_t own[4];                 // E8M0 of this tile's V tiles (FUSED)
   const int64_t bk = blockIdx.x / n_tiles, tile = blockIdx.x - bk * n_tiles;
   const int64_t b = bk / kv_heads, h = bk - b * kv_heads;
   const uint8_t* vts = vtile + bk * n_vtiles;
-  constexpr int CPR = D / 8;
-  for (int vi = threadIdx.x; vi < kKvTile * CPR; vi += 256) {
+  uint4 x[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int vi = threadIdx.x + 256 * i;
+    const int kk = vi / CPR, cc = vi - kk * CPR;
+    const int64_t j = tile * kKvTile + kk;
+    x[i] = j < seq_k ? *reinterpret_cast<const uint4*>(v + b * vs0 + h * vs1 + j * vs2 + cc * 8)
+                     : make_uint4(0, 0, 0, 0);
+  }
+  if constexpr (FUSED) {
+    // absolute maximum of each V tile (up to 4 of R >= 32 rows) of this key tile
+    float am[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int kk = (threadIdx.x + 256 * i) / CPR;
+      const uint32_t ws[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf16_lo(ws[e])), fabsf(bf16_hi(ws[e]))));
+      const int t = kk / R;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) am[q] = fmaxf(am[q], q == t ? m : 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float w = wave_max(am[q]);
+      if ((threadIdx.x & 63) == 0) red[q][threadIdx.x >> 6] = w;
+    }
+    __syncthreads();
+    if (threadIdx.x < 4)
+      own[threadIdx.x] = (uint8_t)(mx_shared_exp(fmaxf(fmaxf(red[threadIdx.x][0], red[threadIdx.x][1]),
+                                                       fmaxf(red[threadIdx.x][2], red[threadIdx.x][3])),
+                                                 8) + 127);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int vi = threadIdx.x + 256 * i;
     const int kk = vi / CPR, cc = vi - kk * CPR;
     const int64_t j = tile * kKvTile + kk;
     uint32_t lo = 0, hi = 0;
     if (j < seq_k) {
-      const uint4 x = *reinterpret_cast<const uint4*>(v + b * vs0 + h * vs1 + j * vs2 + cc * 8);
-      const float inv = exp2i(127 - (int)vts[j / R]);
-      const uint32_t ws[4] = {x.x, x.y, x.z, x.w};
+      const float inv = exp2i(127 - (int)(FUSED ? own[kk / R] : vts[j / R]));
+      const uint32_t ws[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
       uint32_t bb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bb[i] = e4m3_pack2(clamp448(bf16_lo(ws[i]) * inv), clamp448(bf16_hi(ws[i]) * inv), 1.0f);
+      for (int e = 0; e < 4; ++e)
+        bb[e] = e4m3_pack2(clamp448(bf16_lo(ws[e]) * inv), clamp448(bf16_hi(ws[e]) * inv), 1.0f);
       lo = bb[0] | (bb[1] << 16);
       hi = bb[2] | (bb[3] << 16);
     }
@@ -274,7 +316,7 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict_
     for (int blk = 0; blk < 4; ++blk) {
       int64_t j = tile * kKvTile + 32 * blk;
       if (j >= seq_k) j = seq_k - 1;
-      s |= (uint32_t)vts[j / R] << (8 * blk);
+      s |= (uint32_t)(FUSED ? own[(j - tile * kKvTile) / R] : vts[j / R]) << (8 * blk);
     }
     *reinterpret_cast<uint32_t*>(r + TB::K + TB::VS_OFF) = s;
   }
@@ -628,11 +670,17 @@ static hipError_t launch_pack_d(const PrefillParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((pack_k_kernel<D>), dim3((unsigned)((total_k + 255) / 256)), dim3(256), 0, stream, p.k,
                      p.ks[0], p.ks[1], p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, p.ws + L.off_rec, total_k,
                      p.hadamard);
-  hipLaunchKernelGGL((vtile_scale_kernel<D>), dim3((unsigned)(bk * L.n_vtiles)), dim3(256), 0, stream, p.v,
-                     p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_vtiles, wvt);
-  hipLaunchKernelGGL((pack_v_kernel<D>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v, p.vs[0],
-                     p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_tiles, L.n_vtiles, wvt,
-                     p.ws + L.off_rec);
+  if (p.v_tile_rows <= kKvTile) {
+    hipLaunchKernelGGL((pack_v_kernel<D, true>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v,
+                       p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_tiles, L.n_vtiles, wvt,
+                       p.ws + L.off_rec);
+  } else {
+    hipLaunchKernelGGL((vtile_scale_kernel<D>), dim3((unsigned)(bk * L.n_vtiles)), dim3(256), 0, stream, p.v,
+                       p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_vtiles, wvt);
+    hipLaunchKernelGGL((pack_v_kernel<D, false>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v,
+                       p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_tiles, L.n_vtiles, wvt,
+                       p.ws + L.off_rec);
+  }
   return hipGetLastError();
 }
 
