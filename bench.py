@@ -6,7 +6,8 @@ heads, 4096 tokens, head_dim 128, 4 outlier K channels x20): the K/V quantize
 pre-pass plus the attention kernel, which quantizes Q in its prologue.  The
 decode (batch 64, 64/8 heads, 32768 cached tokens) and block-verify (batch 32,
 8 queries over 16384 + 8 cached tokens) workloads are timed in the same run and
-reported as extra objects.  Inputs are seeded and synthetic and resident in HBM
+reported as extra objects, and so is the 131072-token causal prefill (batch 1,
+64 query / 8 KV heads, 2% of K rows x10).  Inputs are seeded and synthetic and resident in HBM
 before timing starts; each workload first runs untimed for half a second so
 that the GPU's clocks settle, then W warmup steps, then K timed steps.
 
@@ -169,6 +170,49 @@ def bench_prefill(torch, ops, synth, steps, warmup):
     del ppw
     return dict(w=w, wall_ms=wall * 1e3 / steps, pack_ms=pack_ms, attn_ms=attn_ms, flops=flops, pairs=pairs,
                 fast_ms=fast_ms, had=had, swa=dict(ms=swa_ms, flops=swa_flops))
+
+
+def bench_prefill_long(torch, ops, synth, steps, warmup):
+    """The 131072-token causal prefill (batch 1, 64 query / 8 KV heads,
+    head_dim 128, 2% of K rows x10), drawn on the GPU with torch's seeded
+    generator; pack + attention per step, the attention timed separately."""
+    w = synth.WORKLOADS[4]
+    B, Hq, Hkv, N, d = w["B"], w["Hq"], w["Hkv"], w["Nq"], w["d"]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(4000)
+    log("[bench] generating the long causal prefill workload on the GPU")
+    q = torch.randn((B, Hq, N, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, N, d), generator=g, device=dev, dtype=torch.float32)
+    rows = torch.rand((B, Hkv, N, 1), generator=g, device=dev) < w["k_outlier_row_frac"]
+    k = torch.where(rows, k * w["k_outlier_factor"], k).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, N, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    pp = ops.PackedPrefill(q, k, v, causal=True, softmax_scale=1.0 / math.sqrt(d), v_tile_rows=w["v_tile_rows"])
+    stream = torch.cuda.current_stream()
+    pp.pack()
+    pp.attend()
+    for _ in range(warmup):
+        pp.pack()
+        pp.attend()
+    evs = [Events(torch, 3) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        e.record(0, stream)
+        pp.pack(stream)
+        e.record(1, stream)
+        pp.attend(stream)
+        e.record(2, stream)
+    torch.cuda.synchronize()
+    pack_ms = sum(e.ms(0, 1) for e in evs) / steps
+    attn_ms = sum(e.ms(1, 2) for e in evs) / steps
+    assert torch.isfinite(pp.o.float()).all().item(), "non-finite long prefill output"
+    flops = B * Hq * causal_pairs(N, N) * 4.0 * d
+    tf = flops / (attn_ms * 1e-3) / 1e12
+    del pp, q, k, v
+    return dict(workload=w["name"], steps=steps, pack_kv_ms=round(pack_ms, 3), attention_ms=round(attn_ms, 3),
+                algorithmic_flops=flops,
+                value=round(flops / ((pack_ms + attn_ms) * 1e-3) / 1e12, 1), unit="TFLOP/s",
+                attention_tflops=round(tf, 1), frac_of_mixed_peak=round(tf / PEAK_MIXED_TFLOPS, 4))
 
 
 def build_cache(torch, ops, w, seed):
@@ -406,6 +450,9 @@ def main():
         line["block_verify"] = bench_decode(torch, ops, synth, 5, args.steps, args.warmup)
         torch.cuda.empty_cache()
         line["kv_append_prompt"] = bench_append_prefill(torch, ops, synth, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        # ~0.25 s per step: a few steps are enough
+        line["prefill_long"] = bench_prefill_long(torch, ops, synth, min(args.steps, 5), min(args.warmup, 2))
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
