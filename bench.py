@@ -249,9 +249,11 @@ def bench_decode(torch, ops, synth, cfg, steps, warmup):
                      device=q.device)
     stream = torch.cuda.current_stream()
 
-    def timed(window):
-        run = lambda: ops.attn_decode(q, kc, ks, vc, vs, w["kv_len"], v_tile_rows=w["v_tile_rows"], out=o,
-                                      workspace=ws, softmax_scale=1.0 / math.sqrt(w["d"]), window=window)
+    def timed(window, cache=None, paging=None):
+        c = cache or (kc, ks, vc, vs)
+        pg = paging or {}
+        run = lambda: ops.attn_decode(q, *c, w["kv_len"], v_tile_rows=w["v_tile_rows"], out=o, workspace=ws,
+                                      softmax_scale=1.0 / math.sqrt(w["d"]), window=window, **pg)
         settle(torch, run, seconds=SETTLE_S if window == 0 else 0.2)
         for _ in range(warmup):
             run()
@@ -286,6 +288,28 @@ def bench_decode(torch, ops, synth, cfg, steps, warmup):
     gbs_w = nbytes_w / (ms_w * 1e-3) / 1e9
     out["sliding_window"] = dict(window=SWA_WINDOW, us=round(ms_w * 1e3, 2), value=round(gbs_w, 1), unit="GB/s",
                                  bytes=nbytes_w, frac=round(gbs_w / PEAK_HBM_GBS, 4))
+    # the same cache as a paged cache (256-token pages in a shuffled order)
+    P = 256
+    if w["kv_len"] % P == 0:
+        B, Hkv, R = w["B"], w["Hkv"], w["v_tile_rows"]
+        npp = w["kv_len"] // P
+        g = torch.Generator(device=q.device)
+        g.manual_seed(5000 + cfg)
+        perm = torch.randperm(B * npp, generator=g, device=q.device)
+        table = perm.view(B, npp).to(torch.int32)
+
+        def to_pages(t, per):
+            src = t.reshape((B, Hkv, npp, per) + tuple(t.shape[3:])).transpose(1, 2)
+            pool = torch.empty((B * npp, Hkv, per) + tuple(t.shape[3:]), dtype=t.dtype, device=t.device)
+            pool[perm.long()] = src.reshape((B * npp, Hkv, per) + tuple(t.shape[3:]))
+            return pool
+
+        pc = (to_pages(kc, P), to_pages(ks, P), to_pages(vc, P), to_pages(vs, P // R))
+        ms_p = timed(0, pc, dict(block_table=table, page_size=P))
+        gbs_p = nbytes / (ms_p * 1e-3) / 1e9
+        out["paged"] = dict(page_size=P, ms=round(ms_p, 4), value=round(gbs_p, 1), unit="GB/s",
+                            frac=round(gbs_p / PEAK_HBM_GBS, 4))
+        del pc
     # the cache writer of the same step: q_len new tokens per sequence appended
     # at the end of the cache (the last q_len positions are rewritten)
     out["kv_append"] = bench_append(torch, ops, kc, ks, vc, vs, w["B"], w["Hkv"], d, w["q_len"],

@@ -31,6 +31,23 @@ __device__ __forceinline__ int append_len(const AppendParams& p, int b) {
   return (len < 0 || (int64_t)len + p.n_new > p.cap) ? -1 : len;
 }
 
+// Cache row of position pos of (b, h): rows [b][h][cap] in a contiguous
+// cache, [page][h][page_size] in a paged one (page ids from the block table).
+__device__ __forceinline__ int64_t cache_row(const AppendParams& p, int b, int h, int pos) {
+  if (p.block_table == nullptr) return ((int64_t)b * p.kv_heads + h) * p.cap + pos;
+  const int64_t page = p.block_table[(int64_t)b * p.pages_per_seq + pos / p.page_size];
+  return (page * p.kv_heads + h) * p.page_size + pos % p.page_size;
+}
+
+// Index of the E8M0 scale of V tile `tile` (R rows) of (b, h); a page holds
+// whole V tiles.
+__device__ __forceinline__ int64_t vscale_index(const AppendParams& p, int b, int h, int tile) {
+  if (p.block_table == nullptr) return ((int64_t)b * p.kv_heads + h) * p.n_vtiles_cap + tile;
+  const int pos = tile * p.R;
+  const int64_t page = p.block_table[(int64_t)b * p.pages_per_seq + pos / p.page_size];
+  return (page * p.kv_heads + h) * (p.page_size / p.R) + (pos % p.page_size) / p.R;
+}
+
 template <int D>
 __device__ __forceinline__ void append_k(const AppendParams& p, int64_t id, int64_t total) {
   constexpr int NB = D / 32;
@@ -68,7 +85,7 @@ __device__ __forceinline__ void append_k(const AppendParams& p, int64_t id, int6
     }
     scale = mxfp4_quantize32f(x, codes);
   }
-  const int64_t row = ((int64_t)b * p.kv_heads + h) * p.cap + len + t;
+  const int64_t row = cache_row(p, b, h, len + t);
   *reinterpret_cast<uint4*>(p.k_codes + row * (D / 2) + 16 * g) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
   p.k_scales[row * NB + g] = (uint8_t)scale;
 }
@@ -103,14 +120,15 @@ __device__ __forceinline__ void append_v(const AppendParams& p, int64_t wg, int 
     for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(ws[k])), fabsf(bf16_hi(ws[k]))));
   }
   amax = block_max256(amax, red);
-  uint8_t* const scale_ptr = p.v_scales + bh * p.n_vtiles_cap + tile;
+  uint8_t* const scale_ptr = p.v_scales + vscale_index(p, b, h, tile);
   const bool has_old = len > r0;                    // the tile was partly filled before
   int X = mx_shared_exp(amax, 8);
   const int X_old = has_old ? (int)*scale_ptr - 127 : -127;
   const bool requant = has_old && X > X_old;
   X = max(X, X_old);
   const float inv = exp2i(-X);
-  uint8_t* const codes = p.v_codes + (bh * p.cap) * D;
+  // codes of the tile's first row; its rows are consecutive cache rows
+  uint8_t* const codes = p.v_codes + cache_row(p, b, h, r0) * D;
   // re-encode the earlier rows from their bf16 values when the scale grew
   if (requant) {
     const uint16_t* tail = p.v_tail + bh * R * D;
@@ -118,14 +136,14 @@ __device__ __forceinline__ void append_v(const AppendParams& p, int64_t wg, int 
     for (int vi = threadIdx.x; vi < nvec_old; vi += 256) {
       const int i = vi / CPR, cc = vi % CPR;
       const uint4 w = *reinterpret_cast<const uint4*>(tail + (int64_t)i * D + cc * 8);
-      *reinterpret_cast<uint2*>(codes + (int64_t)(r0 + i) * D + cc * 8) = e4m3_quantize8(w, inv);
+      *reinterpret_cast<uint2*>(codes + (int64_t)i * D + cc * 8) = e4m3_quantize8(w, inv);
     }
   }
   for (int vi = threadIdx.x; vi < nvec_new; vi += 256) {
     const int r = first_new + vi / CPR, cc = vi % CPR;
     const uint4 w = *reinterpret_cast<const uint4*>(p.v_new + b * p.vs[0] + (int64_t)(r - len) * p.vs[1] +
                                                     h * p.vs[2] + cc * 8);
-    *reinterpret_cast<uint2*>(codes + (int64_t)r * D + cc * 8) = e4m3_quantize8(w, inv);
+    *reinterpret_cast<uint2*>(codes + (int64_t)(r - r0) * D + cc * 8) = e4m3_quantize8(w, inv);
   }
   if (threadIdx.x == 0) *scale_ptr = (uint8_t)(X + 127);
   if (slot != 0) return;

@@ -59,6 +59,8 @@ struct DecodeArgs {
   float c;          // softmax_scale * log2(e), divided by D for rotated queries
   int hadamard;
   int window;       // > 0: query t sees only the `window` most recent keys up to its position
+  const int32_t* block_table;   // paged cache: page ids [batch][pages_per_seq], or NULL
+  int page_size, pages_per_seq;
 };
 
 template <int D>
@@ -155,10 +157,27 @@ decode_split_kernel(DecodeArgs a) {
                        (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones};
   const int klg = lg & (NB - 1);    // D = 64: lanes of k-blocks 2, 3 reread blocks 0, 1 (their Q is zero)
 
-  const uint8_t* gk = a.kc + bk * (int64_t)a.cap * (D / 2);
-  const uint32_t* gks = reinterpret_cast<const uint32_t*>(a.ksc + bk * (int64_t)a.cap * NB);
-  const uint8_t* gv = a.vc + bk * (int64_t)a.cap * D;
-  const uint8_t* gvs = a.vsc + bk * a.n_vtiles_cap;
+  // Cache row of key j0 (a multiple of 128) of this sequence and KV head, and
+  // the V-scale index of its R-row tile.  Contiguous cache: rows
+  // [bk][cap]; paged cache: rows [page][kv_head][page_size], one page per
+  // page_size keys, and a page (a multiple of 128 keys and of R) holds whole
+  // 128-key tiles and whole V tiles.
+  struct TileRef { int64_t row, vsi; int kmax; };
+  auto tile_ref = [&](int j0_) __attribute__((always_inline)) {
+    TileRef t;
+    if (a.block_table == nullptr) {
+      t.row = bk * (int64_t)a.cap + j0_;
+      t.vsi = bk * a.n_vtiles_cap + j0_ / a.R;
+      t.kmax = min(127, a.cap - 1 - j0_);       // rows past the capacity are not read
+    } else {
+      const int64_t page = a.block_table[(int64_t)b * a.pages_per_seq + j0_ / a.page_size];
+      const int slot = j0_ % a.page_size;
+      t.row = (page * a.kv_heads + kvh) * a.page_size + slot;
+      t.vsi = (page * a.kv_heads + kvh) * (a.page_size / a.R) + slot / a.R;
+      t.kmax = 127;
+    }
+    return t;
+  };
 
   // ---- tile staging: the next tile is held in registers while this one
   // computes, then written to LDS (K rows padded, V chunks XOR-swizzled) ----
@@ -171,11 +190,15 @@ decode_split_kernel(DecodeArgs a) {
   // arrays stay in registers
   auto dload = [&](int tile) __attribute__((always_inline)) {
     const int j0_ = j_begin + tile * 128;
+    const TileRef t = tile_ref(j0_);
+    const uint8_t* gk = a.kc + t.row * (D / 2);
+    const uint32_t* gks = reinterpret_cast<const uint32_t*>(a.ksc + t.row * NB);
+    const uint8_t* gv = a.vc + t.row * D;
     static_for<KPT>([&](auto I) {
       constexpr int i = decltype(I)::value;
       const int ci = tid + i * NT;
       if (KCH % NT == 0 || ci < KCH) {
-        const int key = min(j0_ + ci / NB, a.cap - 1);
+        const int key = min(ci / NB, t.kmax);
         rk[i] = *reinterpret_cast<const v4i*>(gk + (int64_t)key * (D / 2) + (ci % NB) * 16);
       }
     });
@@ -186,7 +209,7 @@ decode_split_kernel(DecodeArgs a) {
       constexpr int i = decltype(I)::value;
       const int ci = tid + i * NT;
       if (VCH % NT == 0 || ci < VCH) {
-        const int key = min(j0_ + ci / NC, a.cap - 1);
+        const int key = min(ci / NC, t.kmax);
         rv[i] = *reinterpret_cast<const v4i*>(gv + (int64_t)key * D + (ci % NC) * 16);
       }
     });
@@ -201,7 +224,7 @@ decode_split_kernel(DecodeArgs a) {
       constexpr int i = decltype(I)::value;
       const int ki = tid + i * NT;
       if (128 % NT == 0 || ki < 128) {
-        const int key = min(j0_ + ki, a.cap - 1);
+        const int key = min(ki, t.kmax);
         rs[i] = NB == 4 ? gks[key] : (uint32_t)reinterpret_cast<const uint16_t*>(gks)[key];
       }
     });
@@ -256,8 +279,9 @@ decode_split_kernel(DecodeArgs a) {
     int psc;
     softmax_tile<ND>(S, a.c, m_run, O, L, Phi, Plo, psc);
     // ---- O^T += V^T · P^T, L += 1 · P^T ----
-    const int vkey = min(j0 + 32 * lg, a.cap - 1);
-    const int vs = (int)gvs[vkey / a.R];
+    // V scale of this lane group's 32 keys (an R-row tile holds whole groups)
+    const TileRef tr = tile_ref(j0);
+    const int vs = (int)a.vsc[tr.vsi + (j0 % a.R + min(32 * lg, tr.kmax)) / a.R];
     const int src_row_in_piece = ql >> 1, src_half = ql & 1;
 #pragma unroll
     for (int dd = 0; dd < ND; ++dd) {
@@ -382,6 +406,7 @@ static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   a.hadamard = p.hadamard;
   a.window = p.window < p.kv_len ? p.window : 0;   // a window of kv_len or more keeps every key
   a.o = p.o; a.lse = p.lse; a.os0 = p.os[0]; a.os1 = p.os[1]; a.os2 = p.os[2]; a.q_heads = p.q_heads;
+  a.block_table = p.block_table; a.page_size = p.page_size; a.pages_per_seq = p.pages_per_seq;
   a.direct = splits == 1 && (reinterpret_cast<uintptr_t>(p.o) & 7) == 0 && p.os[0] % 4 == 0 && p.os[1] % 4 == 0 &&
              p.os[2] % 4 == 0;
   const dim3 grid((unsigned)((int64_t)p.batch * p.kv_heads * splits));

@@ -40,6 +40,15 @@ qk4v8_status from_hip(hipError_t e) { return e == hipSuccess ? QK4V8_OK : QK4V8_
 
 bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
+// A paged cache: pages of page_size keys (a multiple of the 128-key tile and
+// of the V tile), pages_per_seq entries per sequence in the block table, and
+// the per-sequence capacity equal to pages_per_seq * page_size.
+bool valid_paging(const int32_t* block_table, int page_size, int pages_per_seq, int v_tile_rows, int cap) {
+  if (block_table == nullptr) return true;
+  if (page_size < 128 || page_size % 128 != 0 || page_size % v_tile_rows != 0 || pages_per_seq < 1) return false;
+  return (int64_t)page_size * pages_per_seq == cap && (reinterpret_cast<uintptr_t>(block_table) & 3) == 0;
+}
+
 qk4v8_status validate_prefill(const qk4v8_prefill_args* a) {
   if (a == nullptr) return QK4V8_ERR_NULL;
   if (a->batch < 0 || a->q_heads < 1 || a->kv_heads < 1 || a->seq_q < 0 || a->seq_k < 0) return QK4V8_ERR_SHAPE;
@@ -88,6 +97,7 @@ qk4v8_status validate_decode(const qk4v8_decode_args* a) {
   if (!good_scale(a->softmax_scale)) return QK4V8_ERR_SHAPE;
   if (a->hadamard != 0 && a->hadamard != 1) return QK4V8_ERR_SHAPE;
   if (a->window < 0) return QK4V8_ERR_SHAPE;
+  if (!valid_paging(a->block_table, a->page_size, a->pages_per_seq, a->v_tile_rows, a->cap)) return QK4V8_ERR_SHAPE;
   return QK4V8_OK;
 }
 
@@ -229,6 +239,7 @@ qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream) {
   if (a->kv_lens == nullptr && (a->kv_len < 0 || (int64_t)a->kv_len + a->n_new > a->cap)) return QK4V8_ERR_SHAPE;
   if (a->cap > (1 << 30)) return QK4V8_ERR_SHAPE;
   if (a->hadamard != 0 && a->hadamard != 1) return QK4V8_ERR_SHAPE;
+  if (!valid_paging(a->block_table, a->page_size, a->pages_per_seq, a->v_tile_rows, a->cap)) return QK4V8_ERR_SHAPE;
   for (int i = 0; i < 3; ++i)
     if (a->k_stride[i] < 0 || a->k_stride[i] % 8 != 0 || a->v_stride[i] < 0 || a->v_stride[i] % 8 != 0)
       return QK4V8_ERR_STRIDE;
@@ -253,6 +264,7 @@ qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream) {
   p.batch = a->batch; p.kv_heads = a->kv_heads; p.n_new = a->n_new; p.kv_len = a->kv_len; p.cap = a->cap;
   p.head_dim = a->head_dim; p.R = a->v_tile_rows; p.hadamard = a->hadamard;
   p.n_vtiles_cap = (a->cap + a->v_tile_rows - 1) / a->v_tile_rows;
+  p.block_table = a->block_table; p.page_size = a->page_size; p.pages_per_seq = a->pages_per_seq;
   return from_hip(launch_append(p, stream));
 }
 
@@ -273,6 +285,7 @@ qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream) {
   p.num_splits = a->num_splits; p.softmax_scale = a->softmax_scale;
   p.hadamard = a->hadamard;
   p.window = a->window;
+  p.block_table = a->block_table; p.page_size = a->page_size; p.pages_per_seq = a->pages_per_seq;
   p.ws = static_cast<uint8_t*>(a->workspace);
   return from_hip(launch_decode(p, stream));
 }

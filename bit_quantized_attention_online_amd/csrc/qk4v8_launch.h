@@ -55,6 +55,8 @@ struct DecodeParams {
   int batch, q_len, q_heads, kv_heads, kv_len, cap, head_dim, v_tile_rows, num_splits;
   int hadamard;              // 1: queries rotated by H_d (the cache K was written rotated)
   int window;                // sliding window (0: none)
+  const int32_t* block_table;  // paged cache: [batch, pages_per_seq] page ids, or NULL
+  int page_size, pages_per_seq;
   float softmax_scale;
   uint8_t* ws;
 };
@@ -80,6 +82,8 @@ struct AppendParams {
   int batch, kv_heads, n_new, kv_len, cap, head_dim, R;
   int hadamard;              // 1: K rows rotated by H_d before quantization
   int64_t n_vtiles_cap;      // ceil(cap / R)
+  const int32_t* block_table;  // paged cache: [batch, pages_per_seq] page ids, or NULL
+  int page_size, pages_per_seq;
 };
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 

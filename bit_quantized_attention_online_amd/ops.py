@@ -47,7 +47,8 @@ class DecodeArgs(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("v_tile_rows", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("hadamard", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("hadamard", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32)]
 
 
 class AppendArgs(ctypes.Structure):
@@ -57,7 +58,8 @@ class AppendArgs(ctypes.Structure):
                 ("v_scales", ctypes.c_void_p), ("v_tail", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("n_new", ctypes.c_int32),
                 ("kv_len", ctypes.c_int32), ("cap", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("v_tile_rows", ctypes.c_int32), ("hadamard", ctypes.c_int32)]
+                ("v_tile_rows", ctypes.c_int32), ("hadamard", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32)]
 
 
 class QK4V8Error(RuntimeError):
@@ -223,8 +225,18 @@ class PackedPrefill:
         return self.o
 
 
+def _paging(a, block_table, page_size):
+    """Fill the paged-cache fields; returns the per-sequence capacity."""
+    if block_table is None:
+        return None
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise TypeError("block_table must be a contiguous int32 [batch, pages_per_seq] tensor")
+    a.block_table, a.page_size, a.pages_per_seq = block_table.data_ptr(), page_size, block_table.shape[1]
+    return page_size * block_table.shape[1]
+
+
 def _decode_args(q, k_codes, k_scales, v_codes, v_scales, o, lse, kv_len, v_tile_rows, kv_lens, num_splits,
-                 softmax_scale):
+                 softmax_scale, block_table=None, page_size=0):
     B, q_len, Hq, d = q.shape
     _, Hkv, cap, _ = k_codes.shape
     for t in (k_codes, k_scales, v_codes, v_scales):
@@ -243,22 +255,30 @@ def _decode_args(q, k_codes, k_scales, v_codes, v_scales, o, lse, kv_len, v_tile
     a.batch, a.q_len, a.q_heads, a.kv_heads, a.kv_len, a.cap = B, q_len, Hq, Hkv, kv_len, cap
     a.head_dim, a.v_tile_rows, a.num_splits = d, v_tile_rows, num_splits
     a.softmax_scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
+    paged_cap = _paging(a, block_table, page_size)
+    if paged_cap is not None:
+        a.cap = paged_cap
     return a
 
 
-def decode_workspace_bytes(q, k_codes, kv_len, v_tile_rows=256, num_splits=0, window=0):
-    a = _decode_args(q, k_codes, k_codes, k_codes, k_codes, q, None, kv_len, v_tile_rows, None, num_splits, None)
+def decode_workspace_bytes(q, k_codes, kv_len, v_tile_rows=256, num_splits=0, window=0, block_table=None,
+                           page_size=0):
+    a = _decode_args(q, k_codes, k_codes, k_codes, k_codes, q, None, kv_len, v_tile_rows, None, num_splits, None,
+                     block_table, page_size)
     a.window = window
     return lib().qk4v8_decode_workspace_bytes(ctypes.byref(a))
 
 
 def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256, kv_lens=None, num_splits=0,
                 softmax_scale=None, return_lse=False, out=None, workspace=None, stream=None, hadamard=False,
-                window=0):
+                window=0, block_table=None, page_size=0):
     """QK4V8 decode / block verify over a quantized cache.
     q [B, q_len, Hq, d] bf16; k_codes [B, Hkv, cap, d/2], k_scales [B, Hkv, cap, d/32],
     v_codes [B, Hkv, cap, d], v_scales [B, Hkv, ceil(cap/v_tile_rows)] uint8.
     window=W > 0 keeps the W most recent keys of each query.
+    Paged cache: block_table int32 [B, pages_per_seq] and page_size; the cache
+    tensors are then page pools [pages, Hkv, page_size, ...] (v_scales
+    [pages, Hkv, page_size / v_tile_rows]).
     Returns o [B, q_len, Hq, d] bf16 (and lse fp32 [B, q_len, Hq])."""
     _bits16(q)
     o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -266,7 +286,7 @@ def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256
     if kv_lens is not None and kv_lens.dtype != torch.int32:
         raise TypeError("kv_lens must be int32")
     a = _decode_args(q, k_codes, k_scales, v_codes, v_scales, o, lse, kv_len, v_tile_rows, kv_lens, num_splits,
-                     softmax_scale)
+                     softmax_scale, block_table, page_size)
     a.hadamard = int(bool(hadamard))
     a.window = window
     need = lib().qk4v8_decode_workspace_bytes(ctypes.byref(a))
@@ -278,12 +298,13 @@ def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256
 
 
 def kv_append(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows=256,
-              kv_lens=None, stream=None, hadamard=False):
+              kv_lens=None, stream=None, hadamard=False, block_table=None, page_size=0):
     """Quantize n_new tokens per sequence into a decode cache (in place).
     k_new, v_new [B, n_new, Hkv, d] bf16 (token-major, strided); cache tensors as
-    for attn_decode with capacity cap = k_codes.shape[2]; v_tail [B, Hkv, R, d]
-    bf16 keeps the source rows of each sequence's partial V tile.  kv_lens
-    (device int32 [B]) or kv_len: tokens already cached; not modified."""
+    for attn_decode with capacity cap = k_codes.shape[2] (paged: page pools and
+    block_table / page_size as for attn_decode); v_tail [B, Hkv, R, d] bf16
+    keeps the source rows of each sequence's partial V tile.  kv_lens (device
+    int32 [B]) or kv_len: tokens already cached; not modified."""
     _bits16(k_new)
     _bits16(v_new)
     if kv_lens is not None and kv_lens.dtype != torch.int32:
@@ -313,4 +334,7 @@ def kv_append(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len
     a.batch, a.kv_heads, a.n_new, a.kv_len = B, Hkv, n_new, int(kv_len)
     a.cap, a.head_dim, a.v_tile_rows = k_codes.shape[2], d, v_tile_rows
     a.hadamard = int(bool(hadamard))
+    paged_cap = _paging(a, block_table, page_size)
+    if paged_cap is not None:
+        a.cap = paged_cap
     _check(lib().qk4v8_kv_append(ctypes.byref(a), _stream(stream)), "qk4v8_kv_append")

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QK4V8_ABI_VERSION 5
+#define QK4V8_ABI_VERSION 6
 
 typedef enum {
   QK4V8_OK = 0,
@@ -226,6 +226,19 @@ qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t 
  *               q_len + t; the splits cover only the keys from the 128-key tile
  *               holding query 0's first visible key, so the traffic and the
  *               workspace are bounded by W + q_len + 126 keys per sequence.
+ *   block_table, page_size, pages_per_seq : paged cache (vLLM-style blocks of
+ *               whole tiles), or block_table = NULL for the contiguous layout
+ *               above.  Paged: the four cache arrays are page pools
+ *               k_codes [pages, kv_heads, page_size, head_dim/2],
+ *               k_scales [pages, kv_heads, page_size, head_dim/32],
+ *               v_codes [pages, kv_heads, page_size, head_dim],
+ *               v_scales [pages, kv_heads, page_size / v_tile_rows];
+ *               key j of sequence b is slot j % page_size of page
+ *               block_table[b * pages_per_seq + j / page_size] (device int32,
+ *               every entry a sequence reaches must name a valid page).
+ *               page_size is a multiple of 128 and of v_tile_rows, and cap
+ *               must equal pages_per_seq * page_size.  The result is the same
+ *               bits as the contiguous cache holding the same rows.
  */
 typedef struct {
   const uint16_t* q;
@@ -244,6 +257,9 @@ typedef struct {
   size_t workspace_bytes;
   int32_t hadamard;
   int32_t window;
+  const int32_t* block_table;
+  int32_t page_size;
+  int32_t pages_per_seq;
 } qk4v8_decode_args;
 
 /* Workspace bytes qk4v8_attn_decode needs for these sizes (0 on bad sizes). */
@@ -279,6 +295,8 @@ qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream);
  *   no-op); with kv_lens NULL, 0 <= kv_len and kv_len + n_new <= cap.
  *   hadamard     : 1 rotates the new K rows by H_d before quantization (for a
  *                  cache read by qk4v8_attn_decode with hadamard = 1); 0: not.
+ *   block_table, page_size, pages_per_seq : a paged cache, laid out and
+ *                  addressed as in qk4v8_decode_args; NULL: contiguous.
  */
 typedef struct {
   const uint16_t* k_new;
@@ -293,6 +311,9 @@ typedef struct {
   const int32_t* kv_lens;
   int32_t batch, kv_heads, n_new, kv_len, cap, head_dim, v_tile_rows;
   int32_t hadamard;
+  const int32_t* block_table;
+  int32_t page_size;
+  int32_t pages_per_seq;
 } qk4v8_append_args;
 
 qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream);

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.qk4v8_abi_version() == 5
+    assert L.qk4v8_abi_version() == 6
     for s in range(7):
         assert L.qk4v8_status_string(s)
 
@@ -106,6 +106,10 @@ def _decode(**kw):
     (dict(v_tile_rows=16), 2), (dict(num_splits=-1), 2), (dict(v_codes=None), 1),
     (dict(q_stride=[64 * 128, 64 * 128, 100]), 3), (dict(k_codes=4104), 3), (dict(workspace_bytes=0), 5),
     (dict(window=-3), 2),
+    (dict(block_table=4096, page_size=200, pages_per_seq=5, cap=1000), 2),       # not a multiple of 128
+    (dict(block_table=4096, page_size=128, pages_per_seq=8), 2),                 # page < V tile (256)
+    (dict(block_table=4096, page_size=256, pages_per_seq=3), 2),                 # cap != pages * page_size
+    (dict(block_table=4098, page_size=512, pages_per_seq=2), 2),                 # misaligned table
 ])
 def test_decode_validation(kw, status):
     assert ops.lib().qk4v8_attn_decode(ctypes.byref(_decode(**kw)), None) == status
@@ -118,6 +122,24 @@ def test_decode_workspace_query():
     rows = 2 * 8 * 4 * 8
     assert L.qk4v8_decode_workspace_bytes(ctypes.byref(a)) >= rows * (128 * 4 + 4)
     assert L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(q_len=9))) == 0
+
+
+def test_decode_paging_is_validated_by_the_workspace_query():
+    L = ops.lib()
+    ok = _decode(block_table=4096, page_size=512, pages_per_seq=2)        # cap 1024 = 2 pages of 512
+    assert L.qk4v8_decode_workspace_bytes(ctypes.byref(ok)) == L.qk4v8_decode_workspace_bytes(
+        ctypes.byref(_decode()))
+    assert L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(block_table=4096, page_size=384,
+                                                                pages_per_seq=3, cap=1152, v_tile_rows=128))) > 0
+    assert L.qk4v8_decode_workspace_bytes(ctypes.byref(_decode(block_table=4096, page_size=384,
+                                                                pages_per_seq=3, cap=1152))) == 0   # 384 % 256
+
+
+def test_append_paging_validation():
+    L = ops.lib()
+    assert L.qk4v8_kv_append(ctypes.byref(_append(block_table=4096, page_size=200, pages_per_seq=5,
+                                                  cap=1000)), None) == 2
+    assert L.qk4v8_kv_append(ctypes.byref(_append(block_table=4096, page_size=256, pages_per_seq=3)), None) == 2
 
 
 def test_decode_window_bounds_the_splits():
