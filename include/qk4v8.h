@@ -216,7 +216,10 @@ qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t 
  *   1 <= q_len <= kv_len <= cap; (q_heads / kv_heads) * q_len <= 64.
  *   num_splits: KV splits per (batch, kv-head), 0 = chosen by the library.
  *   workspace : at least qk4v8_decode_workspace_bytes() bytes, 256-byte aligned
- *               (fp32 partial outputs and log-sum-exps of the splits).
+ *               (fp32 partial outputs and log-sum-exps of the splits; with a
+ *               single split and an 8-byte aligned o whose strides are
+ *               multiples of 4, o and lse are written directly and the
+ *               workspace is not touched).
  *   hadamard  : 1 when the cache's K rows were rotated before quantization
  *               (qk4v8_kv_append with hadamard = 1); the queries are then
  *               rotated the same way and the scores multiplied by
@@ -226,9 +229,9 @@ qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t 
  *               q_len + t; the splits cover only the keys from the 128-key tile
  *               holding query 0's first visible key, so the traffic and the
  *               workspace are bounded by W + q_len + 126 keys per sequence.
- *   block_table, page_size, pages_per_seq : paged cache (vLLM-style blocks of
- *               whole tiles), or block_table = NULL for the contiguous layout
- *               above.  Paged: the four cache arrays are page pools
+ *   block_table, page_size, pages_per_seq : paged cache (pages of whole tiles
+ *               named per sequence by a block table), or block_table = NULL
+ *               for the contiguous layout above.  Paged: the four cache arrays are page pools
  *               k_codes [pages, kv_heads, page_size, head_dim/2],
  *               k_scales [pages, kv_heads, page_size, head_dim/32],
  *               v_codes [pages, kv_heads, page_size, head_dim],
