@@ -30,10 +30,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__host__ __device__ constexpr int subtile_key(int t, int r) {
-  return (t >> 2) * 64 + 16 * (r >> 2) + 4 * (t & 3) + (r & 3);
-}
-
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef v2i __attribute__((address_space(3))) * lds_v2i_ptr;
 

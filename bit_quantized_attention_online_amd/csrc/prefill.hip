@@ -62,14 +62,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds_base + 16*l (lds_base is wave-uniform).  Completion is tracked by
-// vmcnt, not by the compiler.
-__device__ __forceinline__ void global_to_lds16(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                   reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                       reinterpret_cast<uintptr_t>(lds_base)),
-                                   16, 0, 0);
+// 16 bytes per lane from global memory straight into LDS through a buffer
+// resource (MUBUF load with the LDS bit): lane l copies bytes voffset ..
+// voffset + 15 of the `bytes`-long range at `base` (wave-uniform) to lds_base
+// + 16*l (lds_base wave-uniform); reads past the range return zeros.
+// Completion is tracked by vmcnt, not by the compiler.  The compiler counts
+// these in vmcnt only, so the LDS reads of the MFMA step keep exact lgkmcnt
+// waits; with the FLAT-encoded global_load_lds it waits for every
+// outstanding LDS read instead, which defeats the operand prefetch.
+__device__ __forceinline__ void buffer_to_lds16(const uint8_t* base, uint32_t bytes, uint32_t voffset,
+                                                uint8_t* lds_base) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_base)), 16,
+      voffset, 0, 0, 0);
 }
 
 // Workgroup barrier inside the attention loop.  The LDS data it orders comes
@@ -405,7 +412,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const uint32_t row_span = (uint32_t)max(row_lim - row_low, 0);
 
   const int64_t bk = (int64_t)b * a.kv_heads + kvh;
-  const uint8_t* const grec = a.rec + (bk * a.n_tiles + t0) * TB::REC + lane * 16;
+  const uint8_t* const grec = a.rec + (bk * a.n_tiles + t0) * TB::REC;   // wave-uniform
 
   // ---- Q prologue: this wave's 32 rows to MXFP4 in registers; lane (q, h)
   // holds head_dim block 2s + h of row q for contraction step s ----
@@ -487,7 +494,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     static_for<(TB::CHUNKS + kWaves - 1) / kWaves>([&](auto I) {
       constexpr int i = decltype(I)::value;
       const int c = wave + kWaves * i;
-      if (kWaves * (i + 1) <= TB::CHUNKS || c < TB::CHUNKS) global_to_lds16(src + c * 1024, dst + c * 1024);
+      if (kWaves * (i + 1) <= TB::CHUNKS || c < TB::CHUNKS)
+        buffer_to_lds16(src, TB::REC, (uint32_t)(c * 1024 + lane * 16), dst + c * 1024);
     });
   };
   // wait until at most `pending` of this wave's direct loads are in flight

@@ -12,6 +12,10 @@
 //    NOT saturate (an overflow becomes NaN), so callers clamp to +-448 first.
 //    The sign of a zero result is kept.
 //  * v_cvt_scalef32_pk_f32_fp8 computes decode(code) * scale.
+//  * The unscaled v_cvt_pk_fp8_f32 / v_cvt_pk_f32_fp8 use the same OCP E4M3
+//    code (RNE).  Measured issue cost with four waves per SIMD: the E4M3
+//    conversions and v_exp_f32 take about 2.7x the cycles of an fp32 FMA,
+//    except the unscaled E4M3 -> f32 back conversion (about 1.6x).
 //  * v_mfma_scale_f32_16x16x128_f8f6f4: lane l holds row/column (l % 16) and
 //    supplies the E8M0 scale of block (l / 16) (32 consecutive k) for that
 //    row/column.  With fp4 operands lane l holds k = 32*(l/16) + j in nibble j
@@ -187,6 +191,15 @@ __device__ __forceinline__ void hadamard_stage_lane_xor32(float (&x)[32], bool u
   }
 }
 
+// Key (0..127 of a 128-key tile) behind row r of QK^T subtile t in the
+// 16x16x128 layout.  S^T = K·Q^T puts row 4*(l/16) + i of the 16x16 result in
+// element i of lane l, so lane l holds the keys 64*(t/4) + 16*(l/16) +
+// 4*(t%4) + i of its query: with the FP8 operand order above, dword t of the
+// P·V operand built from them needs no lane exchange.
+__host__ __device__ constexpr int subtile_key(int t, int r) {
+  return (t >> 2) * 64 + 16 * (r >> 2) + 4 * (t & 3) + (r & 3);
+}
+
 // Scaled MFMA wrappers.  `sa`/`sb` hold E8M0 bytes; OPA/OPB select the byte.
 template <int FA, int FB, int OPA = 0, int OPB = 0>
 __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
@@ -205,6 +218,14 @@ __device__ __forceinline__ uint32_t e4m3_put2(uint32_t old, float a, float b, fl
   v2s o = __builtin_bit_cast(v2s, old);
   o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, scale, HI);
   return __builtin_bit_cast(uint32_t, o);
+}
+
+// The same without a scale (RNE to E4M3 of the values themselves): the
+// unscaled E4M3 <-> f32 conversions run faster than the scaled ones for the
+// back conversion, and the P split works on p / 2^X directly.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_put2_unscaled(uint32_t old, float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
 
 // Causal / window / length mask: the score of the key at offset x survives
@@ -264,7 +285,7 @@ __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run,
   const float m_new = fmaxf(m_run, tmax);
   // wave-uniform, rarely taken: move the running max only when it grew by more
   // than kLazyRescale somewhere in the wave
-  const bool grow = __builtin_amdgcn_readfirstlane((int)__any(m_new > m_run + kLazyRescale)) != 0;
+  const bool grow = __builtin_amdgcn_ballot_w64(m_new > m_run + kLazyRescale) != 0;
   if (__builtin_expect(grow, 0)) {
     const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
@@ -275,23 +296,25 @@ __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run,
   const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
   const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
   psc = X + 127;
-  const float sh = exp2i(X), sl = exp2i(X - 4);
+  // p / 2^X = 2^(s*c - (m_use + X)): the range scale folds into the
+  // exponent, so hi and its back conversion need no scale operand
+  const float mX = m_use + (float)X;
   // independent passes over the 32 scores, in place: weights, hi codes (the
   // previous tile's codes are dead here and are overwritten), residuals, lo
-  // codes
+  // codes (lo = E4M3(16 * residual), the scaled convert's 2^-4)
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[t][i] = __builtin_amdgcn_exp2f(fmaf(S[t][i], c, -m_use));
+    for (int i = 0; i < 4; ++i) S[t][i] = __builtin_amdgcn_exp2f(fmaf(S[t][i], c, -mX));
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const uint32_t h = e4m3_put2<false>((uint32_t)Phi[t], S[t][0], S[t][1], sh);
-    Phi[t] = (int)e4m3_put2<true>(h, S[t][2], S[t][3], sh);
+    const uint32_t h = e4m3_put2_unscaled<false>((uint32_t)Phi[t], S[t][0], S[t][1]);
+    Phi[t] = (int)e4m3_put2_unscaled<true>(h, S[t][2], S[t][3]);
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)Phi[t], sh, false);
-    const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)Phi[t], sh, true);
+    const auto b01 = __builtin_amdgcn_cvt_pk_f32_fp8(Phi[t], false);
+    const auto b23 = __builtin_amdgcn_cvt_pk_f32_fp8(Phi[t], true);
     S[t][0] -= b01[0];
     S[t][1] -= b01[1];
     S[t][2] -= b23[0];
@@ -299,8 +322,8 @@ __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run,
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const uint32_t l = e4m3_put2<false>((uint32_t)Plo[t], S[t][0], S[t][1], sl);
-    Plo[t] = (int)e4m3_put2<true>(l, S[t][2], S[t][3], sl);
+    const uint32_t l = e4m3_put2<false>((uint32_t)Plo[t], S[t][0], S[t][1], 0.0625f);
+    Plo[t] = (int)e4m3_put2<true>(l, S[t][2], S[t][3], 0.0625f);
   }
 }
 
@@ -330,7 +353,7 @@ __device__ __forceinline__ void softmax_tile32(v16f (&S)[4], float c, float& m_r
   const float mx = max_with_lane_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
   const float tmax = mx * c;
   const float m_new = fmaxf(m_run, tmax);
-  const bool grow = __builtin_amdgcn_readfirstlane((int)__any(m_new > m_run + kLazyRescale)) != 0;
+  const bool grow = __builtin_amdgcn_ballot_w64(m_new > m_run + kLazyRescale) != 0;
   if (__builtin_expect(grow, 0)) {
     const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
@@ -341,42 +364,42 @@ __device__ __forceinline__ void softmax_tile32(v16f (&S)[4], float c, float& m_r
   const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
   const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
   psc = X + 127;
-  const float sh = exp2i(X), sl = exp2i(X - 4);
-  // p = 2^(s*c - m), in place
+  const float mX = m_use + (float)X;
+  // p / 2^X = 2^(s*c - (m_use + X)), in place
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) S[kb][i] = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -m_use));
+    for (int i = 0; i < 16; ++i) S[kb][i] = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -mX));
   // hi = E4M3(p / 2^X)
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int dw = 4 * (kb & 1) + w;
-      uint32_t h = e4m3_put2<false>((uint32_t)Phi[kb >> 1][dw], S[kb][4 * w], S[kb][4 * w + 1], sh);
-      Phi[kb >> 1][dw] = (int)e4m3_put2<true>(h, S[kb][4 * w + 2], S[kb][4 * w + 3], sh);
+      uint32_t h = e4m3_put2_unscaled<false>((uint32_t)Phi[kb >> 1][dw], S[kb][4 * w], S[kb][4 * w + 1]);
+      Phi[kb >> 1][dw] = (int)e4m3_put2_unscaled<true>(h, S[kb][4 * w + 2], S[kb][4 * w + 3]);
     }
-  // residual p - hi * 2^X, in place
+  // residual p / 2^X - hi, in place
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t h = (uint32_t)Phi[kb >> 1][4 * (kb & 1) + w];
-      const auto b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, false);
-      const auto b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sh, true);
+      const int h = Phi[kb >> 1][4 * (kb & 1) + w];
+      const auto b01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+      const auto b23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
       S[kb][4 * w] -= b01[0];
       S[kb][4 * w + 1] -= b01[1];
       S[kb][4 * w + 2] -= b23[0];
       S[kb][4 * w + 3] -= b23[1];
     }
-  // lo = E4M3(residual / 2^(X-4))
+  // lo = E4M3(16 * residual) (scale 2^-4)
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int dw = 4 * (kb & 1) + w;
-      uint32_t l = e4m3_put2<false>((uint32_t)Plo[kb >> 1][dw], S[kb][4 * w], S[kb][4 * w + 1], sl);
-      Plo[kb >> 1][dw] = (int)e4m3_put2<true>(l, S[kb][4 * w + 2], S[kb][4 * w + 3], sl);
+      uint32_t l = e4m3_put2<false>((uint32_t)Plo[kb >> 1][dw], S[kb][4 * w], S[kb][4 * w + 1], 0.0625f);
+      Plo[kb >> 1][dw] = (int)e4m3_put2<true>(l, S[kb][4 * w + 2], S[kb][4 * w + 3], 0.0625f);
     }
 }
 
@@ -402,7 +425,7 @@ __device__ __forceinline__ void softmax_tile32_single(v16f (&S)[4], float c, flo
   const float mx = max_with_lane_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
   const float tmax = mx * c;
   const float m_new = ceilf(fmaxf(m_run, tmax));           // integral (or -inf)
-  const bool grow = __builtin_amdgcn_readfirstlane((int)__any(m_new > m_run + kLazyRescale)) != 0;
+  const bool grow = __builtin_amdgcn_ballot_w64(m_new > m_run + kLazyRescale) != 0;
   if (__builtin_expect(grow, 0)) {
     // 2^(m_run - m_new) built from its exponent bits: exact
     const float alpha = (m_run == -INFINITY) ? 0.0f : exp2i((int)fmaxf(m_run - m_new, -126.0f));
@@ -414,18 +437,18 @@ __device__ __forceinline__ void softmax_tile32_single(v16f (&S)[4], float c, flo
   const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
   const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
   psc = X + 127;
-  const float sh = exp2i(X);
+  const float mX = m_use + (float)X;   // integral: p / 2^X exactly
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) S[kb][i] = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -m_use));
+    for (int i = 0; i < 16; ++i) S[kb][i] = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -mX));
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int dw = 4 * (kb & 1) + w;
-      uint32_t h = e4m3_put2<false>((uint32_t)Phi[kb >> 1][dw], S[kb][4 * w], S[kb][4 * w + 1], sh);
-      Phi[kb >> 1][dw] = (int)e4m3_put2<true>(h, S[kb][4 * w + 2], S[kb][4 * w + 3], sh);
+      uint32_t h = e4m3_put2_unscaled<false>((uint32_t)Phi[kb >> 1][dw], S[kb][4 * w], S[kb][4 * w + 1]);
+      Phi[kb >> 1][dw] = (int)e4m3_put2_unscaled<true>(h, S[kb][4 * w + 2], S[kb][4 * w + 3]);
     }
 }
 
