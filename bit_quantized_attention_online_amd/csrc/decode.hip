@@ -310,7 +310,7 @@ decode_split_kernel(DecodeArgs a) {
     for (int dd = 0; dd < ND; ++dd) {
       const v4f v = O[dd] * inv;
       *reinterpret_cast<uint2*>(orow + dd * 16 + 4 * lg) =
-          make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+          make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
     }
     if (a.lse != nullptr && lg == 0)
       a.lse[((int64_t)b * a.q_len + qt) * a.q_heads + head] = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;

@@ -30,6 +30,9 @@
 //     need no cross-lane transposes.  The 32x32x64 shape keeps the matrix
 //     core busy long enough per instruction for the vector ALU work of the
 //     other wave on the SIMD to issue alongside it.
+#include <algorithm>
+#include <climits>
+
 #include "qk4v8_device.h"
 #include "qk4v8_launch.h"
 
@@ -339,29 +342,45 @@ struct AttnArgs {
   const uint8_t* rec;      // packed tile records [bk][tile]
   int64_t qs0, qs1, qs2, os0, os1, os2;
   int q_heads, kv_heads, group, heads_per_wg, pos_blocks, seq_q, seq_k;
-  int xblocks, pos_groups;   // 1-D grid = pos_groups x xblocks, xblocks fastest
+  int xblocks, pos_groups;   // work items = pos_groups x xblocks, xblocks fastest
   int64_t n_tiles;
   float c;          // softmax_scale * log2(e), divided by D for rotated Q/K
   int hadamard;     // Q (and the packed K) rotated by H_D
   int window;       // causal only: > 0 keeps the `window` most recent keys of each row
 };
 
+// Persistent schedule.  The grid holds one workgroup per CU; workgroup w
+// walks the work items (batch, KV head, head group, position block) in rounds
+// of G = gridDim.x, item w of round 0, item G - 1 - w of round 1, and so on:
+// items come longest first (causal), and the alternating order evens out the
+// rounds (each workgroup starts at a different round).  Within an item nothing changes from a one-item workgroup: the waves
+// run the item's tiles t0 .. t0 + nt - 1 as nt + 1 iterations (QK^T only,
+// P·V + QK^T, ..., P·V only).  Across items three things carry over:
+//  * the tile feed is one stream: the direct loads run two tiles ahead of the
+//    QK^T, into the next item's first tiles during the current item's last
+//    iterations, and the LDS stage of a tile is its index in the stream mod 4;
+//  * the next item's query rows are read at the start of the P·V-only
+//    iteration (the score registers are free there) and quantized in its
+//    VALU phase, which also stores the finished item's rows;
+//  * workgroup start-up (and its wait for the first query rows and tiles) is
+//    paid once per CU, not once per item.
+//
 // Ping-pong schedule.  The 8 waves form two groups of 4 (one wave of each on
 // every SIMD).  Per KV tile k a group runs an MFMA step (P·V of tile k-1, then
 // QK^T of tile k) and a VALU step (mask + softmax + FP8 split of tile k),
 // separated by workgroup barriers.  Both groups run the same instruction
 // stream, but group 1 starts one barrier late (group 0 takes one extra barrier
 // at the end), so in every phase one wave per SIMD feeds the matrix core while
-// the other keeps the vector ALU busy.  Tile k is read in phases 2k .. 2k+3.
+// the other keeps the vector ALU busy.
 //
 // Tiles reach LDS by direct global->LDS loads (no registers involved): every
-// wave copies its share of the 1 KB chunks of tile k+2 at the start of its
-// iteration k, into stage (k+2) % 4, whose previous tile k-2 was last read in
-// phase 2k-1.  Before the barrier that ends phase 2k+1 every wave waits until
-// its chunks of tile k+1 have landed (the loads complete in order, so at most
-// its chunks of tile k+2 may still be in flight), which publishes tile k+1
-// before its first QK^T in phase 2k+2.  A tile thus has about three phases to
-// arrive.
+// wave copies its share of the 1 KB chunks of stream tile T+2 at the start of
+// the iteration that runs QK^T on stream tile T, into stage (T+2) % 4, whose
+// previous tile T-2 was last read by the P·V of an earlier iteration.  Before
+// the barrier that ends that iteration's second phase every wave waits until
+// its chunks of tile T+1 have landed (the loads complete in order, so at most
+// its chunks of tile T+2 may still be in flight), which publishes tile T+1
+// before its first QK^T.  A tile thus has about three phases to arrive.
 // FAST: single-term E4M3 probabilities (integral running maximum, no lo term).
 template <int D, bool CAUSAL, bool FAST>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_kernel(AttnArgs a) {
@@ -378,55 +397,145 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int grp = wave >> 2;    // 0: MFMA step first, 1: one phase behind
   const int ql = lane & 31;     // query column of this lane
   const int lh = lane >> 5;     // lane half (k-block of the MFMA operands)
-
-  // workgroup -> (b, kv head, head group); position block reversed so the
-  // longest causal rows start first
   const int hgroups = a.group / a.heads_per_wg;
-  const int bx = (int)(blockIdx.x % (unsigned)a.xblocks);
-  const int hg = bx % hgroups;
-  const int kvh = (bx / hgroups) % a.kv_heads;
-  const int b = bx / (hgroups * a.kv_heads);
-  const int pg = a.pos_groups - 1 - (int)(blockIdx.x / (unsigned)a.xblocks);
-  const int P0 = pg * a.pos_blocks * kRowsPerWave;
   const int hw = wave % a.heads_per_wg, pb = wave / a.heads_per_wg;
-  const int head = kvh * a.group + hg * a.heads_per_wg + hw;
-  const int p0w = P0 + pb * kRowsPerWave;
   const int off = a.seq_k - a.seq_q;
-
-  // every wave walks the workgroup's tiles t0 .. t0 + nt - 1; rows that
-  // cannot see a tile's keys are masked.  With a sliding window the walk
-  // starts at the tile holding the first key the workgroup's first row sees.
   const int W = CAUSAL ? a.window : 0;
-  const int wg_last_row = min(P0 + a.pos_blocks * kRowsPerWave, a.seq_q) - 1;
-  const int kend_wg = CAUSAL ? min(a.seq_k, wg_last_row + off + 1) : a.seq_k;
-  const int t0 = W > 0 ? max(0, P0 + off - W + 1) / kKvTile : 0;
-  const int nt = (kend_wg + kKvTile - 1) / kKvTile - t0;
-  const bool wave_live = p0w < a.seq_q;
-  const int mask_lim = CAUSAL ? min(a.seq_k - 1, p0w + off) : a.seq_k - 1;   // tiles past it need the mask
-  // tiles starting before the window's lower edge of the wave's last row need it too
-  const int mask_low = W > 0 ? p0w + kRowsPerWave + off - W : -1;
-  const int row = p0w + ql;
-  const int row_lim = (CAUSAL ? min(a.seq_k - 1, row + off) : a.seq_k - 1) - 16 * lh;
-  const int row_low = (W > 0 ? max(0, row + off - W + 1) : 0) - 16 * lh;   // first visible key (clamped at 0)
-  // visible keys row_low .. row_low + row_span (rows past seq_q are never stored)
-  const uint32_t row_span = (uint32_t)max(row_lim - row_low, 0);
+  const int n_items = a.xblocks * a.pos_groups;
+  const int G = (int)gridDim.x;
 
-  const int64_t bk = (int64_t)b * a.kv_heads + kvh;
-  const uint8_t* const grec = a.rec + (bk * a.n_tiles + t0) * TB::REC;   // wave-uniform
+  // ---- work items ----
+  const int R = (n_items + G - 1) / G;
+  auto round_item = [&](int r) -> int { return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+  // the workgroup takes its rounds starting at round blockIdx.x mod R, so
+  // workgroups switch items (and read query rows, store output rows) at
+  // different times; seq_item(i) is the i-th item of that sequence (i is
+  // advanced past a round without an item for this workgroup), n_items at the
+  // end
+  auto seq_item = [&](int& i) -> int {
+    for (; i < R; ++i) {
+      const int j = round_item((i + (int)blockIdx.x) % R);
+      if (j < n_items) return j;
+    }
+    return n_items;
+  };
+  // first row of item j's position block, and its tiles t0 .. t0 + nt - 1:
+  // every wave walks them all; rows that cannot see a tile's keys are masked.
+  // With a sliding window the walk starts at the tile holding the first key
+  // the item's first row sees.
+  auto item_p0 = [&](int j) -> int { return (a.pos_groups - 1 - j / a.xblocks) * a.pos_blocks * kRowsPerWave; };
+  auto item_tiles = [&](int j, int& t0_, int& nt_) __attribute__((always_inline)) {
+    const int p0 = item_p0(j);
+    const int last_row = min(p0 + a.pos_blocks * kRowsPerWave, a.seq_q) - 1;
+    const int kend = CAUSAL ? min(a.seq_k, last_row + off + 1) : a.seq_k;
+    t0_ = W > 0 ? max(0, p0 + off - W + 1) / kKvTile : 0;
+    nt_ = (kend + kKvTile - 1) / kKvTile - t0_;
+  };
+  // (batch * kv_heads + kv head) and this wave's query head for item j
+  auto item_bk = [&](int j) -> int64_t {
+    const int bx = j % a.xblocks;
+    return (int64_t)(bx / (hgroups * a.kv_heads)) * a.kv_heads + (bx / hgroups) % a.kv_heads;
+  };
+  auto item_head = [&](int j) -> int {
+    const int bx = j % a.xblocks;
+    return ((bx / hgroups) % a.kv_heads) * a.group + (bx % hgroups) * a.heads_per_wg + hw;
+  };
 
-  // ---- Q prologue: this wave's 32 rows to MXFP4 in registers; lane (q, h)
-  // holds head_dim block 2s + h of row q for contraction step s ----
-  v8i qf[NS];
-  int qsc[NS];
-  {
-    uint32_t w[NS][16];
+  // ---- the current item (set by setup) ----
+  int b, head, t0, nt, p0w, mask_lim, mask_low, row, row_low;
+  uint32_t row_span;
+  uint32_t g0 = 0;   // stream index of the item's first tile
+  auto setup = [&](int j) __attribute__((always_inline)) {
+    const int64_t bk = item_bk(j);
+    b = (int)(bk / a.kv_heads);
+    head = item_head(j);
+    item_tiles(j, t0, nt);
+    p0w = item_p0(j) + pb * kRowsPerWave;
+    mask_lim = CAUSAL ? min(a.seq_k - 1, p0w + off) : a.seq_k - 1;   // tiles past it need the mask
+    // tiles starting before the window's lower edge of the wave's last row need it too
+    mask_low = W > 0 ? p0w + kRowsPerWave + off - W : -1;
+    row = p0w + ql;
+    const int row_lim = (CAUSAL ? min(a.seq_k - 1, row + off) : a.seq_k - 1) - 16 * lh;
+    row_low = (W > 0 ? max(0, row + off - W + 1) : 0) - 16 * lh;   // first visible key (clamped at 0)
+    // visible keys row_low .. row_low + row_span (rows past seq_q are never stored)
+    row_span = (uint32_t)max(row_lim - row_low, 0);
+  };
+  auto stage_of = [&](int k) -> uint32_t { return (g0 + (uint32_t)k) % kStages; };
+
+  // ---- tile feed: direct global->LDS loads of 1 KB chunks, two tiles ahead
+  // of the QK^T along the stream of this workgroup's items; wave w copies
+  // chunks w, w+8, ... of each tile record ----
+  const int my_chunks = (TB::CHUNKS - wave + kWaves - 1) / kWaves;
+  int feed_i = 0, feed_k = 0, feed_t0, feed_nt;
+  int feed_j = seq_item(feed_i);
+  uint32_t feed_g = 0;
+  item_tiles(feed_j, feed_t0, feed_nt);
+  const uint8_t* feed_rec = a.rec + item_bk(feed_j) * a.n_tiles * TB::REC;   // wave-uniform
+  auto feed = [&]() -> bool __attribute__((always_inline)) {
+    if (feed_j >= n_items) return false;
+    const uint8_t* src = feed_rec + (int64_t)(feed_t0 + feed_k) * TB::REC;
+    uint8_t* dst = lds + (feed_g % kStages) * TB::REC;
+    static_for<(TB::CHUNKS + kWaves - 1) / kWaves>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int c = wave + kWaves * i;
+      if (kWaves * (i + 1) <= TB::CHUNKS || c < TB::CHUNKS)
+        buffer_to_lds16(src, TB::REC, (uint32_t)(c * 1024 + lane * 16), dst + c * 1024);
+    });
+    ++feed_g;
+    if (++feed_k == feed_nt) {
+      ++feed_i;
+      feed_j = seq_item(feed_i);
+      feed_k = 0;
+      if (feed_j < n_items) {
+        item_tiles(feed_j, feed_t0, feed_nt);
+        feed_rec = a.rec + item_bk(feed_j) * a.n_tiles * TB::REC;
+      }
+    }
+    return true;
+  };
+  // wait until at most `pending` of this wave's memory operations are in flight
+  auto wait_dma = [&](int pending) __attribute__((always_inline)) {
+    switch (pending) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1>(); break;
+      case 2: wait_vmcnt<2>(); break;
+      case 3: wait_vmcnt<3>(); break;
+      case 4: wait_vmcnt<4>(); break;
+      case 5: wait_vmcnt<5>(); break;
+      case 6: wait_vmcnt<6>(); break;
+      case 7: wait_vmcnt<7>(); break;
+      case 8: wait_vmcnt<8>(); break;
+      case 9: wait_vmcnt<9>(); break;
+      case 10: wait_vmcnt<10>(); break;
+      case 11: wait_vmcnt<11>(); break;
+      case 12: wait_vmcnt<12>(); break;
+      case 13: wait_vmcnt<13>(); break;
+      case 14: wait_vmcnt<14>(); break;
+      case 15: wait_vmcnt<15>(); break;
+      case 16: wait_vmcnt<16>(); break;
+      case 17: wait_vmcnt<17>(); break;
+      case 18: wait_vmcnt<18>(); break;
+      case 19: wait_vmcnt<19>(); break;
+      case 20: wait_vmcnt<20>(); break;
+      case 21: wait_vmcnt<21>(); break;
+      case 22: wait_vmcnt<22>(); break;
+      case 23: wait_vmcnt<23>(); break;
+      default: wait_vmcnt<24>(); break;
+    }
+  };
+
+
+  // ---- query rows: item j's 32 rows of this wave, bf16, lane (q, h) holding
+  // head_dim block 2s + h of row q for contraction step s ----
+  auto load_q = [&](int j, uint32_t (&w)[NS][16]) __attribute__((always_inline)) {
+    const int r = item_p0(j) + pb * kRowsPerWave + ql;
+    const int64_t qbase = (int64_t)(item_bk(j) / a.kv_heads) * a.qs0 + (int64_t)item_head(j) * a.qs1 + (int64_t)r * a.qs2;
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) w[st][i] = 0;
-      if (row < a.seq_q) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.q + b * a.qs0 + (int64_t)head * a.qs1 + row * a.qs2 +
-                                                          32 * (2 * st + lh));
+      if (r < a.seq_q) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.q + qbase + 32 * (2 * st + lh));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint4 x = src[i];
@@ -434,11 +543,16 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
       }
     }
+  };
+  // ... to MXFP4 in MFMA operand registers (rows past seq_q quantize zeros)
+  v8i qf[NS];
+  int qsc[NS];
+  auto quantize_q = [&](uint32_t (&w)[NS][16]) __attribute__((always_inline)) {
     if (!a.hadamard) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         uint32_t c[4] = {0, 0, 0, 0};
-        qsc[st] = row < a.seq_q ? (int)mxfp4_quantize32(w[st], c) : 127;
+        qsc[st] = (int)mxfp4_quantize32(w[st], c);
         qf[st] = fp4_operand(v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]});
       }
     } else {
@@ -467,47 +581,59 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         qf[st] = fp4_operand(v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]});
       }
     }
-  }
+  };
 
   v16f O[NDB];
-  v16f L = v16f{};
+  v16f L;
   v16f S[4];
+  float m_run;
+  auto reset_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) O[db] = v16f{};
-  float m_run = -INFINITY;
+    for (int db = 0; db < NDB; ++db) O[db] = v16f{};
+    L = v16f{};
+    m_run = -INFINITY;
+  };
   v8i Phi[2] = {v8i{}, v8i{}}, Plo[2] = {v8i{}, v8i{}};
   int psc = 127;
-  if (tid < 256) reinterpret_cast<uint32_t*>(lds + kOnes)[tid] = kFp8Ones;
-
-  // output addressing, computed here so the argument block is dead in the loop
-  uint16_t* const orow = a.o + b * a.os0 + (int64_t)head * a.os1 + (int64_t)row * a.os2;
-  float* const lse_row = a.lse ? a.lse + ((int64_t)b * a.q_heads + head) * a.seq_q + row : nullptr;
-  const bool row_live = row < a.seq_q;
   const float cexp = a.c;
 
-  // ---- tile staging: direct global->LDS loads of 1 KB chunks; wave w
-  // copies chunks w, w+8, ... of each tile record ----
-  const int my_chunks = (TB::CHUNKS - wave + kWaves - 1) / kWaves;
-  auto dma = [&](int tile) __attribute__((always_inline)) {
-    const uint8_t* src = grec + (int64_t)tile * TB::REC;
-    uint8_t* dst = lds + (tile % kStages) * TB::REC;
-    static_for<(TB::CHUNKS + kWaves - 1) / kWaves>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      const int c = wave + kWaves * i;
-      if (kWaves * (i + 1) <= TB::CHUNKS || c < TB::CHUNKS)
-        buffer_to_lds16(src, TB::REC, (uint32_t)(c * 1024 + lane * 16), dst + c * 1024);
-    });
-  };
-  // wait until at most `pending` of this wave's direct loads are in flight
-  auto wait_dma = [&](int pending) __attribute__((always_inline)) {
-    switch (pending) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<1>(); break;
-      case 2: wait_vmcnt<2>(); break;
-      case 3: wait_vmcnt<3>(); break;
-      default: wait_vmcnt<4>(); break;
+
+  // ---- store the finished item's rows: normalize by the sum of the
+  // quantized weights, bf16 rows and the log-sum-exp.  Element i of head_dim
+  // block db in lane (q, h) is column 32*db + 8*(i/4) + 4*h + i%4.  Buffer
+  // stores bounded to the rows below seq_q: every wave issues the same
+  // stores and the hardware drops the ones past the bound, so no branch
+  // makes the compiler's vmcnt bookkeeping for the next query rows wait for
+  // the stores to complete. ----
+  auto store_rows = [&]() __attribute__((always_inline)) {
+    const int live_rows = max(0, min(kRowsPerWave, a.seq_q - p0w));
+    const uint16_t* obase = a.o + b * a.os0 + (int64_t)head * a.os1 + (int64_t)p0w * a.os2;
+    const uint32_t obytes = live_rows > 0 ? (uint32_t)(((int64_t)(live_rows - 1) * a.os2 + D) * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(obase), (short)0, (int)obytes, 0x00020000);
+    const uint32_t orow_off = (uint32_t)((int64_t)ql * a.os2 * 2) + 8u * lh;
+    const float l = L[0];     // every row of the ones-MFMA holds the same sum
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint32_t w0 = bf16x2(O[db][4 * g4] * inv, O[db][4 * g4 + 1] * inv);
+        const uint32_t w1 = bf16x2(O[db][4 * g4 + 2] * inv, O[db][4 * g4 + 3] * inv);
+        typedef int v2i_t __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(v2i_t{(int)w0, (int)w1}, ro, orow_off, (32 * db + 8 * g4) * 2, 0);
+      }
+    if (a.lse != nullptr) {
+      // lane half 1 holds the same row: its offset is past the bound
+      float* lbase = a.lse + ((int64_t)b * a.q_heads + head) * a.seq_q + p0w;
+      const __amdgpu_buffer_rsrc_t rl =
+          __builtin_amdgcn_make_buffer_rsrc(lbase, (short)0, live_rows * 4, 0x00020000);
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int((m_use + __log2f(l)) * kLn2), rl,
+                                            lh == 0 ? (uint32_t)ql * 4 : 0x80000000u, 0, 0);
     }
   };
+
 
   // MFMA step k: O^T += V^T·P^T and L += 1·P^T for tile k-1 (FP8 x FP8),
   // then S^T = K·Q^T for tile k (FP4 x FP4; both operands' E8M0 scales are
@@ -523,7 +649,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     v4i kf[4 * NS];
     uint32_t ks[NS];
     auto kload = [&]() __attribute__((always_inline)) {
-      const uint8_t* base = lds + (k % kStages) * TB::REC;
+      const uint8_t* base = lds + stage_of(k) * TB::REC;
       static_for<4 * NS>([&](auto I) {
         constexpr int idx = decltype(I)::value;
         kf[idx] = *reinterpret_cast<const v4i*>(base + (idx * 64 + lane) * 16);
@@ -533,7 +659,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int i = 0; i < NS; ++i) ks[i] = ksw[i];
     };
     if constexpr (PV) {
-      const uint8_t* base = lds + ((k - 1) % kStages) * TB::REC;
+      const uint8_t* base = lds + stage_of(k - 1) * TB::REC;
       const uint8_t* lv = base + TB::K + TB::SC + lane * 16;
       const uint32_t vsw = *reinterpret_cast<const uint32_t*>(base + TB::K + TB::VS_OFF);
       const v4i o0 = *reinterpret_cast<const v4i*>(lds + kOnes + (lane & 31) * 16);
@@ -601,15 +727,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       softmax_tile32<NDB>(S, cexp, m_run, O, L, Phi, Plo, psc);
   };
 
-  // one iteration of the schedule for tile k; the first (no P·V yet) and the
-  // final P·V-only step are peeled so the steady state has no branches
-  auto iteration = [&](int k, auto with_pv, auto with_qk) __attribute__((always_inline)) {
-    const bool prefetch = k + 2 < nt;
-    if (prefetch) dma(k + 2);
-    // tile k+1 must have landed (from this wave) before the barrier that ends
-    // phase 2k+1: group 1's MFMA phase, group 0's VALU phase
-    const int pending = prefetch ? my_chunks : 0;
-    mfma_step(k, with_pv, with_qk);
+  // one iteration of the schedule for tile k of the current item; the first
+  // (no P·V yet) is peeled so the steady state has no branches
+  auto iteration = [&](int k, auto with_pv) __attribute__((always_inline)) {
+    const int pending = feed() ? my_chunks : 0;
+    mfma_step(k, with_pv, std::true_type{});
     // The matrix instructions are pure values to the compiler, which would
     // otherwise sink them past the barrier into the other phase: an empty asm
     // that reads the accumulators keeps them (and the softmax below) on their
@@ -618,50 +740,67 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       static_for<NDB>([&](auto DB) { keep_in_vgprs(O[decltype(DB)::value]); });
       keep_in_vgprs(L);
     }
-    if constexpr (decltype(with_qk)::value) {
-      static_for<4>([&](auto KB) { keep_in_vgprs(S[decltype(KB)::value]); });
-    }
-    if (grp == 1 && k + 1 < nt) wait_dma(pending);
+    static_for<4>([&](auto KB) { keep_in_vgprs(S[decltype(KB)::value]); });
+    // the next tile of the stream must have landed (from this wave) before the
+    // barrier that ends the second phase of this iteration: group 1's MFMA
+    // phase, group 0's VALU phase
+    if (grp == 1) wait_dma(pending);
     phase_barrier();
-    if constexpr (decltype(with_qk)::value) {
-      valu_step(k);
-      static_for<2>([&](auto I) {
-        keep_in_vgprs(Phi[decltype(I)::value]);
-        if constexpr (!FAST) keep_in_vgprs(Plo[decltype(I)::value]);
-      });
-    }
-    if (grp == 0 && k + 1 < nt) wait_dma(pending);
+    valu_step(k);
+    static_for<2>([&](auto I) {
+      keep_in_vgprs(Phi[decltype(I)::value]);
+      if constexpr (!FAST) keep_in_vgprs(Plo[decltype(I)::value]);
+    });
+    if (grp == 0) wait_dma(pending);
     phase_barrier();
   };
-  dma(0);
-  if (nt > 1) dma(1);
-  wait_dma(nt > 1 ? my_chunks : 0);    // tile 0 (this wave's chunks)
+  // the item's last iteration (P·V of tile nt - 1 only): its MFMA phase also
+  // requests the next item's query rows, its VALU phase stores this item's
+  // rows and switches to item jn
+  auto last_iteration = [&](int jn) __attribute__((always_inline)) {
+    uint32_t wq[NS][16];
+    if (jn < n_items) load_q(jn, wq);
+    mfma_step(nt, std::true_type{}, std::false_type{});
+    static_for<NDB>([&](auto DB) { keep_in_vgprs(O[decltype(DB)::value]); });
+    keep_in_vgprs(L);
+    phase_barrier();
+    store_rows();
+    if (jn < n_items) {
+      quantize_q(wq);
+      g0 += (uint32_t)nt;
+      setup(jn);
+      reset_acc();
+    }
+    phase_barrier();
+  };
+
+  // ---- first item: its rows, the stream's first two tiles ----
+  int cur_i = 0;
+  const int cur = seq_item(cur_i);
+  setup(cur);
+  feed();
+  const int pending0 = feed() ? my_chunks : 0;
+  {
+    uint32_t wq[NS][16];
+    load_q(cur, wq);
+    quantize_q(wq);
+  }
+  reset_acc();
+  if (tid < 256) reinterpret_cast<uint32_t*>(lds + kOnes)[tid] = kFp8Ones;
+  wait_dma(pending0);                  // tile 0 (this wave's chunks)
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the ones operand is written
   phase_barrier();
   if (grp == 1) phase_barrier();       // group 1 runs one phase behind
-  iteration(0, std::false_type{}, std::true_type{});
-  for (int k = 1; k < nt; ++k) iteration(k, std::true_type{}, std::true_type{});
-  iteration(nt, std::true_type{}, std::false_type{});
-  if (grp == 0) phase_barrier();       // matches group 1's initial wait
-
-  // ---- epilogue: normalize by the sum of the quantized weights, store bf16
-  // rows and the log-sum-exp.  Element i of head_dim block db in lane (q, h)
-  // is column 32*db + 8*(i/4) + 4*h + i%4. ----
-  if (!wave_live || !row_live) return;
-  const float l = L[0];     // every row of the ones-MFMA holds the same sum
-  const float inv = 1.0f / l;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const uint32_t w0 = f32_to_bf16(O[db][4 * g4] * inv) | (f32_to_bf16(O[db][4 * g4 + 1] * inv) << 16);
-      const uint32_t w1 = f32_to_bf16(O[db][4 * g4 + 2] * inv) | (f32_to_bf16(O[db][4 * g4 + 3] * inv) << 16);
-      *reinterpret_cast<uint2*>(orow + 32 * db + 8 * g4 + 4 * lh) = make_uint2(w0, w1);
-    }
-  if (lse_row != nullptr && lh == 0) {
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    *lse_row = (m_use + __log2f(l)) * kLn2;
+  for (;;) {
+    int next_i = cur_i + 1;
+    const int jn = seq_item(next_i);
+    iteration(0, std::false_type{});
+    for (int k = 1; k < nt; ++k) iteration(k, std::true_type{});
+    last_iteration(jn);
+    if (jn >= n_items) break;
+    cur_i = next_i;
   }
+  if (grp == 0) phase_barrier();       // matches group 1's initial wait
 }
 
 static int gcd_int(int x, int y) {
@@ -714,7 +853,15 @@ static hipError_t launch_attn_d(const PrefillParams& p, hipStream_t stream) {
   const int rows_per_wg = a.pos_blocks * kRowsPerWave;
   a.xblocks = p.batch * p.kv_heads * (a.group / a.heads_per_wg);
   a.pos_groups = (p.seq_q + rows_per_wg - 1) / rows_per_wg;
-  const dim3 grid((unsigned)((int64_t)a.xblocks * a.pos_groups));
+  // persistent: one workgroup per CU (the kernel's LDS and registers allow
+  // no more), each walking its share of the work items
+  const int64_t items = (int64_t)a.xblocks * a.pos_groups;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)std::min<int64_t>(items, std::max(cus, 1)));
   if (p.causal && p.single_term)
     hipLaunchKernelGGL((attn_kernel<D, true, true>), grid, dim3(kWaves * 64), 0, stream, a);
   else if (p.causal)

@@ -95,21 +95,41 @@ __device__ __forceinline__ float clamp448(float y) { return fminf(fmaxf(y, -448.
 
 // Quantize 32 bf16 values held as 16 packed dwords (element 2i in the low half
 // of word i) into 16 bytes of E2M1 codes (4 dwords) and return the scale byte.
+// The block maximum is taken on the bf16 bit patterns (magnitudes of finite
+// bf16 values order as unsigned integers, two per v_pk_max_u16), and the
+// codes come from the packed bf16 pairs through the scaled convert (x / 2^X,
+// RNE, saturating at 6), one instruction per byte.  Blocks with X < -120
+// (only tiny or zero values) take the fp32 route, so a bf16 subnormal never
+// meets the scaled convert.
 __device__ __forceinline__ uint32_t mxfp4_quantize32(const uint32_t (&w)[16], uint32_t (&codes)[4]) {
-  float amax = 0.0f;
+  typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  v2u16 m = __builtin_bit_cast(v2u16, w[0] & 0x7FFF7FFFu);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
-  int X = mx_shared_exp(amax, 2);
-  float inv = exp2i(-X);   // -X in [-127, 127]; X = -127 gives 2^127
+  for (int i = 1; i < 16; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(v2u16, w[i] & 0x7FFF7FFFu));
+  const uint32_t mag = max((uint32_t)m[0], (uint32_t)m[1]);
+  const int X = mx_shared_exp(__uint_as_float(mag << 16), 2);
+  if (X >= -120) {
+    const float scale = exp2i(X);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t ww = w[4 * i + j];
-      c |= e2m1_pack2(bf16_lo(ww) * inv, bf16_hi(ww) * inv) << (8 * j);
+    for (int i = 0; i < 4; ++i) {
+      uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(v2bf, w[4 * i]), scale, 0);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, w[4 * i + 1]), scale, 1);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, w[4 * i + 2]), scale, 2);
+      codes[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, w[4 * i + 3]), scale, 3);
     }
-    codes[i] = c;
+  } else {
+    const float inv = exp2i(-X);   // -X in [121, 127]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t ww = w[4 * i + j];
+        c |= e2m1_pack2(bf16_lo(ww) * inv, bf16_hi(ww) * inv) << (8 * j);
+      }
+      codes[i] = c;
+    }
   }
   return (uint32_t)(X + 127);
 }
@@ -482,6 +502,14 @@ __device__ __forceinline__ uint2 e4m3_quantize8(uint4 w, float inv) {
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two fp32 -> two bf16 (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  const v2bf r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 }  // namespace qk4v8

@@ -32,10 +32,21 @@ __global__ void __launch_bounds__(256) quantize_qk_kernel(const uint16_t* __rest
   amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   const int X = mx_shared_exp(amax, 2);
-  const float inv = exp2i(-X);
   uint32_t c = 0;
+  if (X >= -120) {
+    // the bf16 pairs straight through the scaled convert (x / 2^X), as in
+    // mxfp4_quantize32
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const float scale = exp2i(X);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[0]), scale, 0);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[1]), scale, 1);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[2]), scale, 2);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[3]), scale, 3);
+  } else {
+    const float inv = exp2i(-X);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c |= e2m1_pack2(bf16_lo(ws[i]) * inv, bf16_hi(ws[i]) * inv) << (8 * i);
+    for (int i = 0; i < 4; ++i) c |= e2m1_pack2(bf16_lo(ws[i]) * inv, bf16_hi(ws[i]) * inv) << (8 * i);
+  }
   if (live) {
     *reinterpret_cast<uint32_t*>(codes + row * (d >> 1) + chunk * 4) = c;
     if ((chunk & 3) == 0) scales[row * (d >> 5) + (chunk >> 2)] = (uint8_t)(X + 127);
