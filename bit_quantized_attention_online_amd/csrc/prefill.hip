@@ -407,14 +407,15 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // ---- work items ----
   const int R = (n_items + G - 1) / G;
   auto round_item = [&](int r) -> int { return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
-  // the workgroup takes its rounds starting at round blockIdx.x mod R, so
-  // workgroups switch items (and read query rows, store output rows) at
-  // different times; seq_item(i) is the i-th item of that sequence (i is
-  // advanced past a round without an item for this workgroup), n_items at the
-  // end
+  // the workgroup takes its rounds starting at round (blockIdx.x mod 8) mod
+  // R, so workgroups switch items (and read query rows, store output rows) at
+  // different times, while the workgroups of one XCD (blockIdx.x mod 8) stay
+  // on the same rounds and share their K/V tiles in its L2; seq_item(i) is
+  // the i-th item of that sequence (i is advanced past a round without an
+  // item for this workgroup), n_items at the end
   auto seq_item = [&](int& i) -> int {
     for (; i < R; ++i) {
-      const int j = round_item((i + (int)blockIdx.x) % R);
+      const int j = round_item((i + ((int)blockIdx.x & 7)) % R);
       if (j < n_items) return j;
     }
     return n_items;
@@ -466,30 +467,36 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // of the QK^T along the stream of this workgroup's items; wave w copies
   // chunks w, w+8, ... of each tile record ----
   const int my_chunks = (TB::CHUNKS - wave + kWaves - 1) / kWaves;
-  int feed_i = 0, feed_k = 0, feed_t0, feed_nt;
-  int feed_j = seq_item(feed_i);
-  uint32_t feed_g = 0;
-  item_tiles(feed_j, feed_t0, feed_nt);
-  const uint8_t* feed_rec = a.rec + item_bk(feed_j) * a.n_tiles * TB::REC;   // wave-uniform
+  // feed state: the next record to copy, the copies left in its item, the
+  // LDS stage it goes to (its stream index mod 4)
+  int feed_i = 0;
+  const uint8_t* feed_src = nullptr;
+  int feed_left = 0;
+  uint32_t feed_stage = 0;
+  auto feed_item = [&]() __attribute__((always_inline)) {
+    const int j = seq_item(feed_i);
+    if (j < n_items) {
+      int t0_, nt_;
+      item_tiles(j, t0_, nt_);
+      feed_src = a.rec + (item_bk(j) * a.n_tiles + t0_) * TB::REC;
+      feed_left = nt_;
+    }
+  };
+  feed_item();
   auto feed = [&]() -> bool __attribute__((always_inline)) {
-    if (feed_j >= n_items) return false;
-    const uint8_t* src = feed_rec + (int64_t)(feed_t0 + feed_k) * TB::REC;
-    uint8_t* dst = lds + (feed_g % kStages) * TB::REC;
+    if (feed_left == 0) return false;   // past the last item
+    uint8_t* dst = lds + feed_stage * TB::REC;
     static_for<(TB::CHUNKS + kWaves - 1) / kWaves>([&](auto I) {
       constexpr int i = decltype(I)::value;
       const int c = wave + kWaves * i;
       if (kWaves * (i + 1) <= TB::CHUNKS || c < TB::CHUNKS)
-        buffer_to_lds16(src, TB::REC, (uint32_t)(c * 1024 + lane * 16), dst + c * 1024);
+        buffer_to_lds16(feed_src, TB::REC, (uint32_t)(c * 1024 + lane * 16), dst + c * 1024);
     });
-    ++feed_g;
-    if (++feed_k == feed_nt) {
+    feed_src += TB::REC;
+    feed_stage = (feed_stage + 1) & (kStages - 1);
+    if (--feed_left == 0) {
       ++feed_i;
-      feed_j = seq_item(feed_i);
-      feed_k = 0;
-      if (feed_j < n_items) {
-        item_tiles(feed_j, feed_t0, feed_nt);
-        feed_rec = a.rec + item_bk(feed_j) * a.n_tiles * TB::REC;
-      }
+      feed_item();
     }
     return true;
   };
