@@ -34,6 +34,8 @@ PEAK_MIXED_TFLOPS = 2.0 / (1.0 / PEAK_FP4_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
 SETTLE_S = 0.5                 # untimed sustained load before the warmup steps
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_causal_gqa_n4096_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "bit_quantized_attention_online_amd", "csrc", "prefill.hip")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.json")
+DECODE_SOURCE = os.path.join(ROOT, "bit_quantized_attention_online_amd", "csrc", "decode.hip")
 
 
 def log(*a):
@@ -43,6 +45,20 @@ def log(*a):
 def source_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(path, source, key=None):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when the kernel source changed since it was taken."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256_16") != source_hash(source):
+        return None
+    if key is not None:
+        t = t.get("workloads", {}).get(key, {})
+    return t.get("bytes_per_launch")
 
 
 def causal_pairs(nq, nk, window=0):
@@ -280,7 +296,8 @@ def bench_decode(torch, ops, synth, cfg, steps, warmup):
     gbs = nbytes / (ms * 1e-3) / 1e9
     out = dict(workload=w["name"], value=round(gbs, 1), unit="GB/s", ms=round(ms, 4), bytes=nbytes,
                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                             frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+                             frac=round(gbs / PEAK_HBM_GBS, 4),
+                             traffic=measured_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCE, w["name"])))
     # the drafter's sliding window over the same cache: the keys some query of
     # a sequence can see (window + q_len - 1) are the algorithmic bytes
     ms_w = timed(SWA_WINDOW)
@@ -423,12 +440,7 @@ def main():
     step_ms = pf["pack_ms"] + pf["attn_ms"]
     value = pf["flops"] / (step_ms * 1e-3) / 1e12
     attn_tflops = pf["flops"] / (pf["attn_ms"] * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        if t.get("source_sha256_16") == source_hash(ATTN_SOURCE):
-            traffic = t.get("bytes_per_launch")
+    traffic = measured_traffic(TRAFFIC_FILE, ATTN_SOURCE)
     line = {
         "metric": "QK4V8 attn: prefill TFLOP/s + decode KV GB/s, % of MI355X roofline",
         "value": round(value, 2),
