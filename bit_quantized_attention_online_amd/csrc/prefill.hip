@@ -141,13 +141,11 @@ PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, i
 //   scales: [lane][kb*NS + s]                         at K
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict__ k, int64_t ks0, int64_t ks1,
-                                                     int64_t ks2, int kv_heads, int seq_k, int64_t n_tiles,
-                                                     uint8_t* __restrict__ rec, int64_t total, int hadamard) {
+__device__ __forceinline__ void pack_k_block(const uint16_t* __restrict__ k, int64_t ks0, int64_t ks1, int64_t ks2,
+                                             int kv_heads, int seq_k, int64_t n_tiles, uint8_t* __restrict__ rec,
+                                             int hadamard, int64_t id) {
   using TB = TileBytes<D>;
   constexpr int NB = D / 32, NS = D / 64;
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= total) return;
   const int g = (int)(id % NB);
   const int64_t jj = (id / NB) % (n_tiles * kKvTile);
   const int64_t bk = id / (NB * n_tiles * kKvTile);
@@ -192,6 +190,14 @@ __global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict_
   r[TB::K + lane * (4 * NS) + kb * NS + step] = (uint8_t)scale;
 }
 
+template <int D>
+__global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict__ k, int64_t ks0, int64_t ks1,
+                                                     int64_t ks2, int kv_heads, int seq_k, int64_t n_tiles,
+                                                     uint8_t* __restrict__ rec, int64_t total, int hadamard) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id < total) pack_k_block<D>(k, ks0, ks1, ks2, kv_heads, seq_k, n_tiles, rec, hadamard, id);
+}
+
 // ---------------------------------------------------------------------------
 // Pre-pass 2: E8M0 scale of each V tile of R rows (absmax over R x D).
 // One workgroup (256 threads) per (group, tile).
@@ -234,19 +240,27 @@ __global__ void __launch_bounds__(256) vtile_scale_kernel(const uint16_t* __rest
 // FUSED (V tiles of R <= 128 rows, which never straddle a 128-key tile): the
 // workgroup computes the scales of its own V tiles from the rows it holds in
 // registers instead of reading them from the vtile_scale pre-pass.
+template <int D>
+struct PackVShared {
+  static constexpr int LDSROW = D + 4;   // bytes per key row in LDS (padding spreads banks)
+  uint8_t tileb[kKvTile * LDSROW];
+  float red[4][4];
+  uint8_t own[4];                        // E8M0 of this tile's V tiles (FUSED)
+};
+
 template <int D, bool FUSED>
-__global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict__ v, int64_t vs0, int64_t vs1,
-                                                     int64_t vs2, int kv_heads, int seq_k, int R, int64_t n_tiles,
-                                                     int64_t n_vtiles, const uint8_t* __restrict__ vtile,
-                                                     uint8_t* __restrict__ rec) {
+__device__ __forceinline__ void pack_v_tile(const uint16_t* __restrict__ v, int64_t vs0, int64_t vs1, int64_t vs2,
+                                            int kv_heads, int seq_k, int R, int64_t n_tiles, int64_t n_vtiles,
+                                            const uint8_t* __restrict__ vtile, uint8_t* __restrict__ rec,
+                                            int64_t blk, PackVShared<D>& sh) {
   using TB = TileBytes<D>;
-  constexpr int LDSROW = D + 4;   // bytes per key row in LDS (padding spreads banks)
+  constexpr int LDSROW = PackVShared<D>::LDSROW;
   constexpr int CPR = D / 8;
   constexpr int PER = kKvTile * CPR / 256;   // 16-byte chunks per thread (rows tid/CPR + (256/CPR)*i)
-  __shared__ uint8_t tileb[kKvTile * LDSROW];
-  __shared__ float red[4][4];
-  __shared__ uint8_t own[4];                 // E8M0 of this tile's V tiles (FUSED)
-  const int64_t bk = blockIdx.x / n_tiles, tile = blockIdx.x - bk * n_tiles;
+  uint8_t* tileb = sh.tileb;
+  float (*red)[4] = sh.red;
+  uint8_t* own = sh.own;
+  const int64_t bk = blk / n_tiles, tile = blk - bk * n_tiles;
   const int64_t b = bk / kv_heads, h = bk - b * kv_heads;
   const uint8_t* vts = vtile + bk * n_vtiles;
   uint4 x[PER];
@@ -330,6 +344,41 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict_
     }
     *reinterpret_cast<uint32_t*>(r + TB::K + TB::VS_OFF) = s;
   }
+}
+
+template <int D, bool FUSED>
+__global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict__ v, int64_t vs0, int64_t vs1,
+                                                     int64_t vs2, int kv_heads, int seq_k, int R, int64_t n_tiles,
+                                                     int64_t n_vtiles, const uint8_t* __restrict__ vtile,
+                                                     uint8_t* __restrict__ rec) {
+  __shared__ PackVShared<D> sh;
+  pack_v_tile<D, FUSED>(v, vs0, vs1, vs2, kv_heads, seq_k, R, n_tiles, n_vtiles, vtile, rec, blockIdx.x, sh);
+}
+
+// Both packs in one launch (V tiles of R <= 128 rows, whose scales the V
+// workgroups compute themselves): the first nblk_k workgroups pack K, the
+// rest pack one V tile each, so V work starts as K workgroups retire and
+// the step pays one launch instead of two.
+struct PackKVArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t ks0, ks1, ks2, vs0, vs1, vs2;
+  int kv_heads, seq_k, R, hadamard;
+  int64_t n_tiles, n_vtiles, total_k, nblk_k;
+  const uint8_t* vtile;    // unused by the V workgroups here (they compute their scales)
+  uint8_t* rec;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) pack_kv_kernel(PackKVArgs a) {
+  __shared__ PackVShared<D> sh;
+  if ((int64_t)blockIdx.x < a.nblk_k) {
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id < a.total_k) pack_k_block<D>(a.k, a.ks0, a.ks1, a.ks2, a.kv_heads, a.seq_k, a.n_tiles, a.rec, a.hadamard, id);
+    return;
+  }
+  pack_v_tile<D, true>(a.v, a.vs0, a.vs1, a.vs2, a.kv_heads, a.seq_k, a.R, a.n_tiles, a.n_vtiles, a.vtile, a.rec,
+                       (int64_t)blockIdx.x - a.nblk_k, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -821,14 +870,18 @@ static hipError_t launch_pack_d(const PrefillParams& p, hipStream_t stream) {
   uint8_t* wvt = p.ws + L.off_vtile;
   const int64_t bk = (int64_t)p.batch * p.kv_heads;
   const int64_t total_k = bk * L.n_tiles * kKvTile * (D / 32);
-  hipLaunchKernelGGL((pack_k_kernel<D>), dim3((unsigned)((total_k + 255) / 256)), dim3(256), 0, stream, p.k,
-                     p.ks[0], p.ks[1], p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, p.ws + L.off_rec, total_k,
-                     p.hadamard);
+  const int64_t nblk_k = (total_k + 255) / 256;
   if (p.v_tile_rows <= kKvTile) {
-    hipLaunchKernelGGL((pack_v_kernel<D, true>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v,
-                       p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_tiles, L.n_vtiles, wvt,
-                       p.ws + L.off_rec);
+    PackKVArgs a;
+    a.k = p.k; a.v = p.v;
+    a.ks0 = p.ks[0]; a.ks1 = p.ks[1]; a.ks2 = p.ks[2]; a.vs0 = p.vs[0]; a.vs1 = p.vs[1]; a.vs2 = p.vs[2];
+    a.kv_heads = p.kv_heads; a.seq_k = p.seq_k; a.R = p.v_tile_rows; a.hadamard = p.hadamard;
+    a.n_tiles = L.n_tiles; a.n_vtiles = L.n_vtiles; a.total_k = total_k; a.nblk_k = nblk_k;
+    a.vtile = wvt; a.rec = p.ws + L.off_rec;
+    hipLaunchKernelGGL((pack_kv_kernel<D>), dim3((unsigned)(nblk_k + bk * L.n_tiles)), dim3(256), 0, stream, a);
   } else {
+    hipLaunchKernelGGL((pack_k_kernel<D>), dim3((unsigned)nblk_k), dim3(256), 0, stream, p.k, p.ks[0], p.ks[1],
+                       p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, p.ws + L.off_rec, total_k, p.hadamard);
     hipLaunchKernelGGL((vtile_scale_kernel<D>), dim3((unsigned)(bk * L.n_vtiles)), dim3(256), 0, stream, p.v,
                        p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_vtiles, wvt);
     hipLaunchKernelGGL((pack_v_kernel<D, false>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v,

@@ -200,3 +200,34 @@ def test_decode_single_split_direct_and_merged_agree(gpu):
     ro, _ = oatt.qk4v8_decode(q, rkc, rks, rvc.reshape(B, Hkv, n, d), rvs.reshape(B, Hkv, -1), np.array([n] * B), R,
                               1 / math.sqrt(d))
     assert_attn_close(from_dev_bf16(o1), ro, "decode one split")
+
+
+@pytest.mark.parametrize("q_len,d,R", [(1, 128, 64), (8, 128, 256), (3, 64, 32)])
+def test_decode_ignores_cache_bytes_past_each_length(gpu, q_len, d, R):
+    """Rows at or past a sequence's length hold NaN bytes (E4M3 NaN codes,
+    E8M0 NaN scales) in a contiguous cache; the loads stop at the length, so
+    the result is finite and matches the oracle over the valid rows.  The
+    lengths end inside 128-key tiles and inside V tiles."""
+    from bit_quantized_attention_online_amd import ops
+    B, Hq, Hkv, cap = 3, 16, 2, 700
+    rng = np.random.default_rng(91 + q_len + d + R)
+    k = synth.bf16_bits(rng.standard_normal((B, Hkv, cap, d)).astype(np.float32))
+    v = synth.bf16_bits(rng.standard_normal((B, Hkv, cap, d)).astype(np.float32))
+    q = synth.bf16_bits(rng.standard_normal((B, q_len, Hq, d)).astype(np.float32))
+    lens = np.array([700, 333, 129], dtype=np.int32)
+    print(f"[case] decode past-length NaN bytes q_len{q_len} d{d} R{R}", flush=True)
+    kc, ks, vc, vs = _cache_from(k, v, R)
+    rkc, rks = quant.quantize_qk(k)
+    rvc, rvs = quant.quantize_v(v.reshape(B * Hkv, cap, d), R)
+    for b, n in enumerate(lens):
+        kc[b, :, n:] = 0xFF
+        ks[b, :, n:] = 0xFF
+        vc[b, :, n:] = 0xFF
+        vs[b, :, -(-int(n) // R):] = 0xFF          # V tiles that start past the length
+    o = ops.attn_decode(to_dev(q), kc, ks, vc, vs, cap, v_tile_rows=R, kv_lens=torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    out = from_dev_bf16(o)
+    assert np.isfinite(out).all()
+    ro, _ = oatt.qk4v8_decode(q, rkc, rks, rvc.reshape(B, Hkv, cap, d), rvs.reshape(B, Hkv, -1), lens, R,
+                              1 / math.sqrt(d))
+    assert_attn_close(out, ro, "decode past-length NaN bytes")
