@@ -338,15 +338,20 @@ decode_split_kernel(DecodeArgs a) {
   if (lg == 0) a.part_lse[prow] = empty ? -INFINITY : (m_run + __log2f(l));
 }
 
-// One workgroup of D threads per (batch, KV head, query row): combine the
-// splits' partials with weights 2^(lse_s - max).
+// Combine the splits' partials with weights 2^(lse_s - max).  A query row
+// is D/4 threads of four elements each (16-byte partial loads, one 8-byte
+// bf16 store when the output allows it); a workgroup of 256 threads covers
+// 256 / (D/4) rows.
 template <int D>
-__global__ void __launch_bounds__(D) decode_merge_kernel(const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_lse, int kv_heads, int group,
-                                                         int M, int splits, uint16_t* __restrict__ o, int64_t os0,
-                                                         int64_t os1, int64_t os2, float* __restrict__ lse,
-                                                         int q_heads, int q_len) {
-  const int64_t r = blockIdx.x;               // (bk, mrow)
+__global__ void __launch_bounds__(256) decode_merge_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_lse, int kv_heads, int group,
+                                                           int M, int splits, int64_t rows, uint16_t* __restrict__ o,
+                                                           int64_t os0, int64_t os1, int64_t os2, int aligned8,
+                                                           float* __restrict__ lse, int q_heads, int q_len) {
+  constexpr int TPR = D / 4;
+  const int64_t r = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // (bk, mrow)
+  if (r >= rows) return;
+  const int e = (threadIdx.x % TPR) * 4;
   const int64_t bk = r / M;
   const int mrow = (int)(r - bk * M);
   const int b = (int)(bk / kv_heads), kvh = (int)(bk - (int64_t)b * kv_heads);
@@ -354,17 +359,24 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(const float* __restrict
   const float* pl = part_lse + bk * splits * M + mrow;
   float mx = -INFINITY;
   for (int s = 0; s < splits; ++s) mx = fmaxf(mx, pl[(int64_t)s * M]);
-  float wsum = 0.f, acc = 0.f;
+  float wsum = 0.f;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   if (mx != -INFINITY) {
     for (int s = 0; s < splits; ++s) {
       const float w = __builtin_amdgcn_exp2f(pl[(int64_t)s * M] - mx);
       wsum += w;
-      acc += w * part_o[((bk * splits + s) * M + mrow) * D + threadIdx.x];
+      acc += w * *reinterpret_cast<const v4f*>(part_o + ((bk * splits + s) * M + mrow) * D + e);
     }
   }
-  const float val = wsum > 0.f ? acc / wsum : 0.f;
-  o[b * os0 + qt * os1 + (int64_t)head * os2 + threadIdx.x] = (uint16_t)f32_to_bf16(val);
-  if (lse != nullptr && threadIdx.x == 0)
+  const v4f val = wsum > 0.f ? acc / wsum : v4f{0.f, 0.f, 0.f, 0.f};
+  uint16_t* dst = o + b * os0 + qt * os1 + (int64_t)head * os2 + e;
+  if (aligned8) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2(val[0], val[1]), bf16x2(val[2], val[3]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = (uint16_t)f32_to_bf16(val[i]);
+  }
+  if (lse != nullptr && e == 0)
     lse[((int64_t)b * q_len + qt) * q_heads + head] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
@@ -431,9 +443,13 @@ static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((int64_t)p.batch * p.kv_heads * M)), dim3(D), 0,
-                     stream, a.part_o, a.part_lse, p.kv_heads, G, M, splits, p.o, p.os[0], p.os[1], p.os[2], p.lse,
-                     p.q_heads, p.q_len);
+  const int64_t mrows = (int64_t)p.batch * p.kv_heads * M;
+  constexpr int rows_per_wg = 256 / (D / 4);
+  const int aligned8 = (reinterpret_cast<uintptr_t>(p.o) & 7) == 0 && p.os[0] % 4 == 0 && p.os[1] % 4 == 0 &&
+                       p.os[2] % 4 == 0;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((mrows + rows_per_wg - 1) / rows_per_wg)), dim3(256),
+                     0, stream, a.part_o, a.part_lse, p.kv_heads, G, M, splits, mrows, p.o, p.os[0], p.os[1], p.os[2],
+                     aligned8, p.lse, p.q_heads, p.q_len);
   return hipGetLastError();
 }
 
