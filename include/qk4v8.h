@@ -209,7 +209,9 @@ qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t 
  *   v_codes  : uint8 [batch, kv_heads, cap, head_dim]     (E4M3FN, as qk4v8_quantize_v)
  *   v_scales : uint8 [batch, kv_heads, ceil(cap / v_tile_rows)]
  *   kv_lens  : device int32 [batch] with q_len <= kv_lens[b] <= kv_len, or NULL
- *              for every sequence having kv_len entries.
+ *              for every sequence having kv_len entries.  Cache rows at or
+ *              past a sequence's length are never read (their bytes, and the
+ *              V scales of tiles that start there, may be anything).
  *   o        : out bf16 [batch, q_len, q_heads, head_dim], strides o_stride
  *   lse      : out fp32 [batch, q_len, q_heads] contiguous, natural log; may be NULL.
  *   head_dim ∈ {64, 128}; v_tile_rows ∈ {32, 64, 128, 256};
