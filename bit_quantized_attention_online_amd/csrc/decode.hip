@@ -266,6 +266,13 @@ decode_split_kernel(DecodeArgs a) {
     __syncthreads();            // this tile visible
     dload();
 
+    // Wave priorities (workgroups of several waves, three resident per
+    // SIMD): a wave issuing its QK^T reads and MFMAs runs at priority 1, one
+    // issuing P·V at 2, the softmax at 0, so the matrix sections of the
+    // waves on a SIMD go first and its vector work fills the gaps (block
+    // verify 182 -> 175 us; a single-wave decode workgroup is alone on its
+    // SIMD and skips this).
+    if constexpr (MB >= 2) __builtin_amdgcn_s_setprio(1);
     // ---- S^T = K · Q^T ----
     v4f S[8];
 #pragma unroll
@@ -275,6 +282,7 @@ decode_split_kernel(DecodeArgs a) {
       const int sa = (int)((reinterpret_cast<const uint32_t*>(lks)[key] >> (8 * klg)) & 0xFF);
       S[t] = mfma16x16x128<kFmtFp4, kFmtFp4>(af, qf, v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc);
     }
+    if constexpr (MB >= 2) __builtin_amdgcn_s_setprio(0);
     // ---- mask: keys past this row's limit (covers kv_len and the causal
     // block) or, with a window, before its first visible key ----
     if (j0 + 127 > kvlen - a.q_len || !row_ok || (a.window > 0 && j0 < kvlen - a.window)) {
@@ -289,6 +297,7 @@ decode_split_kernel(DecodeArgs a) {
     // ---- online softmax + two-term FP8 P ----
     int psc;
     softmax_tile<ND>(S, a.c, m_run, O, L, Phi, Plo, psc);
+    if constexpr (MB >= 2) __builtin_amdgcn_s_setprio(2);
     // ---- O^T += V^T · P^T, L += 1 · P^T ----
     const int vs = lvs[lg];
     const int src_row_in_piece = ql >> 1, src_half = ql & 1;
@@ -308,6 +317,7 @@ decode_split_kernel(DecodeArgs a) {
     }
     L = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Phi, L, 127, psc);
     L = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Plo, L, 127, psc - 4);
+    if constexpr (MB >= 2) __builtin_amdgcn_s_setprio(0);
   };
 
   dload();
