@@ -29,6 +29,8 @@ DEC_CASES = [
     (2, 8, 2, 1, 777, 800, 128, 64, 5, True),
     (2, 16, 2, 4, 600, 700, 128, 256, 3, True),     # block verify, 32 rows
     (1, 64, 8, 8, 1500, 1536, 128, 256, 0, False),  # 64 rows per KV head
+    (2, 12, 2, 7, 500, 520, 128, 64, 0, True),      # 42 rows: three 16-row blocks
+    (1, 10, 2, 8, 300, 300, 64, 32, 2, False),      # 40 rows at head_dim 64
     (2, 4, 4, 1, 300, 300, 64, 32, 0, False),
     (1, 6, 2, 3, 130, 140, 64, 128, 2, True),
     (2, 8, 8, 1, 1, 1, 128, 256, 0, False),         # a single cached token
