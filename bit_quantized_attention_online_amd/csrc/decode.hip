@@ -22,12 +22,16 @@
 // only the most recent 1024 keys): the splits cover the keys from the tile
 // holding the first query's first visible key to the end of the sequence, so
 // the work and the traffic do not grow with the length of the cache.
+#include <atomic>
+
 #include "qk4v8_device.h"
 #include "qk4v8_launch.h"
 
 namespace qk4v8 {
 
 namespace {
+
+constexpr int kMaxDevices = 64;   // device ordinals the per-device caches cover
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -80,14 +84,6 @@ __device__ __forceinline__ int vswz(int row, int chunk) {
   return chunk ^ (row & (DecTile<D>::NC - 1));
 }
 
-// Resident workgroups per CU (4 SIMDs x waves per SIMD / MB), from the
-// kernels' register use: at head_dim 128 one wave per SIMD for MB = 1, 2
-// (the next tile is staged in registers), two for MB = 3 and three for MB = 4
-// (register budget 168); at head_dim 64 two for MB <= 3 and three for MB = 4.
-__host__ __device__ constexpr int decode_wgs_per_cu(int D, int MB) {
-  return MB == 4 ? 3 : (D == 128 ? (MB == 3 ? 8 : 4) : 8) / MB;
-}
-
 template <int D, int MB>
 __global__ void __launch_bounds__(MB * 64) __attribute__((amdgpu_waves_per_eu(MB == 4 ? 3 : 1, 8)))
 decode_split_kernel(DecodeArgs a) {
@@ -105,7 +101,12 @@ decode_split_kernel(DecodeArgs a) {
   const int s = blockIdx.x % a.splits;
   const int64_t bk = blockIdx.x / a.splits;
   const int b = (int)(bk / a.kv_heads), kvh = (int)(bk - (int64_t)b * a.kv_heads);
-  const int kvlen = a.kv_lens ? a.kv_lens[b] : a.kv_len;
+  // a length outside [q_len, kv_len] is outside the contract: above kv_len
+  // it is clamped to kv_len, so every read stays inside the cache's capacity
+  // (and a paged sequence inside its block-table row); below q_len the
+  // sequence is empty (zero output rows, lse -inf)
+  int kvlen = a.kv_lens ? a.kv_lens[b] : a.kv_len;
+  kvlen = kvlen > a.kv_len ? a.kv_len : (kvlen < a.q_len ? 0 : kvlen);
   // first key of the range the splits share: 0, or with a window the start of
   // the tile holding query 0's first visible key
   const int j_base = a.window > 0 ? max(0, kvlen - a.q_len + 1 - a.window) & ~127 : 0;
@@ -390,27 +391,50 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const float* __restri
     lse[((int64_t)b * q_len + qt) * q_heads + head] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
-int decode_key_span(int kv_len, int q_len, int window) {
-  // with a window the range starts at most 127 keys before query 0's first key
-  if (window > 0 && (int64_t)window + q_len + 126 < kv_len) return window + q_len + 126;
-  return kv_len;
+// Workgroups of decode_split_kernel<D, MB> the current device holds at once:
+// its CU count times the runtime's occupancy figure for the compiled kernel
+// (register and LDS use), so a different compiler, register budget or device
+// partition changes the split count with it.  Cached per device ordinal (a
+// read-only property of the device and the loaded code); 0 when a query fails.
+template <int D, int MB>
+static int64_t decode_capacity_of(int dev) {
+  static std::atomic<int64_t> cache[kMaxDevices];
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&decode_split_kernel<D, MB>), MB * 64, 0) != hipSuccess)
+    return 0;
+  const int64_t c = (int64_t)cus * per_cu;
+  if (c > 0 && dev >= 0 && dev < kMaxDevices) cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+static int64_t decode_capacity(int head_dim, int MB) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (head_dim == 64) {
+    switch (MB) {
+      case 1: return decode_capacity_of<64, 1>(dev);
+      case 2: return decode_capacity_of<64, 2>(dev);
+      case 3: return decode_capacity_of<64, 3>(dev);
+      default: return decode_capacity_of<64, 4>(dev);
+    }
+  }
+  switch (MB) {
+    case 1: return decode_capacity_of<128, 1>(dev);
+    case 2: return decode_capacity_of<128, 2>(dev);
+    case 3: return decode_capacity_of<128, 3>(dev);
+    default: return decode_capacity_of<128, 4>(dev);
+  }
 }
 
 int decode_num_splits(int batch, int kv_heads, int rows, int head_dim, int span, int requested) {
-  const int tiles = (span + 127) / 128;
-  if (requested > 0) return requested < tiles ? requested : tiles;
-  // one round of workgroups: as many as the 256 CUs hold at once (a second,
-  // partial round and larger split partials cost more than they balance),
-  // each with >= 8 tiles of work (below that the merge pass costs more than
-  // the parallelism gains; one split writes the output without it)
-  const int MB = rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 48 ? 3 : 4;
-  const int64_t units = (int64_t)batch * kv_heads;
-  const int64_t capacity = 256 * (int64_t)decode_wgs_per_cu(head_dim, MB);
-  int s = (int)((capacity + units / 2) / units);
-  const int max_s = tiles / 8 > 0 ? tiles / 8 : 1;
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  return s;
+  const int64_t capacity = requested > 0 ? 0 : decode_capacity(head_dim, decode_row_blocks(rows));
+  return decode_split_count((int64_t)batch * kv_heads, span, capacity, requested);
 }
 
 size_t decode_workspace_bytes(int batch, int q_len, int q_heads, int kv_heads, int head_dim, int splits) {

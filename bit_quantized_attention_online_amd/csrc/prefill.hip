@@ -650,7 +650,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     m_run = -INFINITY;
   };
   v8i Phi[2] = {v8i{}, v8i{}}, Plo[2] = {v8i{}, v8i{}};
-  int psc = 127;
+  // E8M0 range exponent of the probabilities this lane supplies for P·V
+  // steps 0 and 1 (the MFMA applies lane half h's byte to k-block h, the
+  // keys 64*s2 + 32*h .. +31)
+  int psc[2] = {127, 127};
   const float cexp = a.c;
 
 
@@ -739,15 +742,15 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         if constexpr (j == NDB && QK) kload();
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (j < NDB) {
-          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][0], Phi[0], O[j], vsc0, psc);
-          if constexpr (!FAST) O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][0], Plo[0], O[j], vsc0, psc - 4);
-          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][1], Phi[1], O[j], vsc1, psc);
-          if constexpr (!FAST) O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][1], Plo[1], O[j], vsc1, psc - 4);
+          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][0], Phi[0], O[j], vsc0, psc[0]);
+          if constexpr (!FAST) O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][0], Plo[0], O[j], vsc0, psc[0] - 4);
+          O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][1], Phi[1], O[j], vsc1, psc[1]);
+          if constexpr (!FAST) O[j] = mfma32x32x64<kFmtFp8, kFmtFp8>(av[j & 1][1], Plo[1], O[j], vsc1, psc[1] - 4);
         } else {
-          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[0], L, 127, psc);
-          if constexpr (!FAST) L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[0], L, 127, psc - 4);
-          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[1], L, 127, psc);
-          if constexpr (!FAST) L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[1], L, 127, psc - 4);
+          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[0], L, 127, psc[0]);
+          if constexpr (!FAST) L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[0], L, 127, psc[0] - 4);
+          L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Phi[1], L, 127, psc[1]);
+          if constexpr (!FAST) L = mfma32x32x64<kFmtFp8, kFmtFp8>(ones, Plo[1], L, 127, psc[1] - 4);
         }
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -778,7 +781,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int i = 0; i < 16; ++i) S[kb][i] = mask_range(S[kb][i], 32 * kb + i, low, row_span);
     }
     if constexpr (FAST)
-      softmax_tile32_single<NDB>(S, cexp, m_run, O, L, Phi, psc);
+      softmax_tile32_single<NDB>(S, cexp, m_run, O, L, Phi, psc, lh);
     else
       softmax_tile32<NDB>(S, cexp, m_run, O, L, Phi, Plo, psc);
   };

@@ -106,7 +106,8 @@ int decode_splits(const qk4v8_decode_args* a) {
                            decode_key_span(a->kv_len, a->q_len, a->window), a->num_splits);
 }
 
-qk4v8_status validate_decode_memory(const qk4v8_decode_args* a) {
+// Buffers of a decode call; *need receives the split partials' bytes.
+qk4v8_status validate_decode_memory(const qk4v8_decode_args* a, size_t* need) {
   if (!a->q || !a->k_codes || !a->k_scales || !a->v_codes || !a->v_scales || !a->o) return QK4V8_ERR_NULL;
   for (int i = 0; i < 3; ++i)
     if (a->q_stride[i] < 0 || a->q_stride[i] % 8 != 0 || a->o_stride[i] < 0) return QK4V8_ERR_STRIDE;
@@ -117,10 +118,11 @@ qk4v8_status validate_decode_memory(const qk4v8_decode_args* a) {
   if (a->lse && !aligned(a->lse, 4)) return QK4V8_ERR_STRIDE;
   if (a->q_heads > 1 && a->o_stride[2] < a->head_dim) return QK4V8_ERR_STRIDE;
   if (a->q_len > 1 && a->o_stride[1] < a->head_dim) return QK4V8_ERR_STRIDE;
+  const int splits = decode_splits(a);
+  if (splits < 1) return QK4V8_ERR_HIP;   // the device's occupancy query failed
+  *need = decode_workspace_bytes(a->batch, a->q_len, a->q_heads, a->kv_heads, a->head_dim, splits);
   if (a->workspace == nullptr || !aligned(a->workspace, kWsAlign)) return QK4V8_ERR_WORKSPACE;
-  const size_t need =
-      decode_workspace_bytes(a->batch, a->q_len, a->q_heads, a->kv_heads, a->head_dim, decode_splits(a));
-  if (a->workspace_bytes < need) return QK4V8_ERR_WORKSPACE;
+  if (a->workspace_bytes < *need) return QK4V8_ERR_WORKSPACE;
   return QK4V8_OK;
 }
 
@@ -180,6 +182,29 @@ size_t qk4v8_prefill_workspace_bytes(const qk4v8_prefill_args* a) {
 
 namespace {
 
+qk4v8_status run_decode(const qk4v8_decode_args* a, hipStream_t stream) {
+  qk4v8_status st = validate_decode(a);
+  if (st != QK4V8_OK) return st;
+  if (a->batch == 0) return QK4V8_OK;
+  size_t need = 0;
+  st = validate_decode_memory(a, &need);
+  if (st != QK4V8_OK) return st;
+  st = check_device();
+  if (st != QK4V8_OK) return st;
+  DecodeParams p;
+  p.q = a->q; p.k_codes = a->k_codes; p.k_scales = a->k_scales; p.v_codes = a->v_codes; p.v_scales = a->v_scales;
+  p.kv_lens = a->kv_lens; p.o = a->o; p.lse = a->lse;
+  for (int i = 0; i < 3; ++i) { p.qs[i] = a->q_stride[i]; p.os[i] = a->o_stride[i]; }
+  p.batch = a->batch; p.q_len = a->q_len; p.q_heads = a->q_heads; p.kv_heads = a->kv_heads; p.kv_len = a->kv_len;
+  p.cap = a->cap; p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows;
+  p.num_splits = a->num_splits; p.softmax_scale = a->softmax_scale;
+  p.hadamard = a->hadamard;
+  p.window = a->window;
+  p.block_table = a->block_table; p.page_size = a->page_size; p.pages_per_seq = a->pages_per_seq;
+  p.ws = static_cast<uint8_t*>(a->workspace);
+  return from_hip(launch_decode(p, stream));
+}
+
 enum PrefillPart { kPack = 1, kAttn = 2 };
 
 qk4v8_status run_prefill(const qk4v8_prefill_args* a, hipStream_t stream, int parts) {
@@ -228,7 +253,9 @@ qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t 
 
 size_t qk4v8_decode_workspace_bytes(const qk4v8_decode_args* a) {
   if (validate_decode(a) != QK4V8_OK) return 0;
-  return decode_workspace_bytes(a->batch, a->q_len, a->q_heads, a->kv_heads, a->head_dim, decode_splits(a));
+  const int splits = decode_splits(a);
+  if (splits < 1) return 0;
+  return decode_workspace_bytes(a->batch, a->q_len, a->q_heads, a->kv_heads, a->head_dim, splits);
 }
 
 qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream) {
@@ -269,25 +296,7 @@ qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream) {
 }
 
 qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream) {
-  qk4v8_status st = validate_decode(a);
-  if (st != QK4V8_OK) return st;
-  if (a->batch == 0) return QK4V8_OK;
-  st = validate_decode_memory(a);
-  if (st != QK4V8_OK) return st;
-  st = check_device();
-  if (st != QK4V8_OK) return st;
-  DecodeParams p;
-  p.q = a->q; p.k_codes = a->k_codes; p.k_scales = a->k_scales; p.v_codes = a->v_codes; p.v_scales = a->v_scales;
-  p.kv_lens = a->kv_lens; p.o = a->o; p.lse = a->lse;
-  for (int i = 0; i < 3; ++i) { p.qs[i] = a->q_stride[i]; p.os[i] = a->o_stride[i]; }
-  p.batch = a->batch; p.q_len = a->q_len; p.q_heads = a->q_heads; p.kv_heads = a->kv_heads; p.kv_len = a->kv_len;
-  p.cap = a->cap; p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows;
-  p.num_splits = a->num_splits; p.softmax_scale = a->softmax_scale;
-  p.hadamard = a->hadamard;
-  p.window = a->window;
-  p.block_table = a->block_table; p.page_size = a->page_size; p.pages_per_seq = a->pages_per_seq;
-  p.ws = static_cast<uint8_t*>(a->workspace);
-  return from_hip(launch_decode(p, stream));
+  return run_decode(a, stream);
 }
 
 }  // extern "C"

@@ -357,7 +357,7 @@ __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run,
 // instructions behind independent work.
 template <int NO>
 __device__ __forceinline__ void softmax_tile32(v16f (&S)[4], float c, float& m_run, v16f (&O)[NO], v16f& L,
-                                               v8i (&Phi)[2], v8i (&Plo)[2], int& psc) {
+                                               v8i (&Phi)[2], v8i (&Plo)[2], int (&psc)[2]) {
   // row maximum: four independent chains, then a tree
   float m4[4];
 #pragma unroll
@@ -383,7 +383,7 @@ __device__ __forceinline__ void softmax_tile32(v16f (&S)[4], float c, float& m_r
   }
   const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
   const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
-  psc = X + 127;
+  psc[0] = psc[1] = X + 127;   // one range exponent per (row, tile)
   const float mX = m_use + (float)X;
   // p / 2^X = 2^(s*c - (m_use + X)), in place
 #pragma unroll
@@ -424,14 +424,19 @@ __device__ __forceinline__ void softmax_tile32(v16f (&S)[4], float c, float& m_r
 }
 
 // Single-term variant of softmax_tile32 (fast mode): P is one E4M3 term per
-// weight.  The running maximum is kept integral, so every rescale is an exact
-// power of two and the E4M3 rounding of p / 2^X = 2^(s*c - floor(tmax) + 7)
-// depends only on the scores and on the tile's maximum, not on when the
-// maximum moved: the result is the same for any order of the tiles.
+// weight, with one E8M0 range exponent per row and aligned 32-key block (the
+// MX block size).  Key block kb of the tile (keys 32*kb .. 32*kb + 31) is
+// S[kb] of this lane and of lane ^ 32, so its maximum takes one lane swap;
+// P·V step s2 applies lane half h's exponent to key block 2*s2 + h.  The
+// running maximum is kept integral, so every rescale is an exact power of
+// two, and the E4M3 rounding of p / 2^X_B = 2^(s*c - floor(max_B) + 7)
+// depends only on the scores and on the block's maximum, not on when the
+// running maximum moved: the result is the same for any order of the tiles
+// and any tiling that keeps the aligned 32-key blocks whole.
 template <int NO>
 __device__ __forceinline__ void softmax_tile32_single(v16f (&S)[4], float c, float& m_run, v16f (&O)[NO], v16f& L,
-                                                      v8i (&Phi)[2], int& psc) {
-  float m4[4];
+                                                      v8i (&Phi)[2], int (&psc)[2], int lh) {
+  float bm[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     float a = fmaxf(S[kb][0], S[kb][1]), b = fmaxf(S[kb][2], S[kb][3]);
@@ -440,9 +445,9 @@ __device__ __forceinline__ void softmax_tile32_single(v16f (&S)[4], float c, flo
       a = fmaxf(a, fmaxf(S[kb][i], S[kb][i + 1]));
       b = fmaxf(b, fmaxf(S[kb][i + 2], S[kb][i + 3]));
     }
-    m4[kb] = fmaxf(a, b);
+    bm[kb] = max_with_lane_xor32(fmaxf(a, b));   // the whole 32-key block of this row
   }
-  const float mx = max_with_lane_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+  const float mx = fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3]));
   const float tmax = mx * c;
   const float m_new = ceilf(fmaxf(m_run, tmax));           // integral (or -inf)
   const bool grow = __builtin_amdgcn_ballot_w64(m_new > m_run + kLazyRescale) != 0;
@@ -455,13 +460,17 @@ __device__ __forceinline__ void softmax_tile32_single(v16f (&S)[4], float c, flo
     m_run = m_new;
   }
   const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-  const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
-  psc = X + 127;
-  const float mX = m_use + (float)X;   // integral: p / 2^X exactly
+  int X[4];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < 4; ++kb) X[kb] = (int)floorf(fmaxf(bm[kb] * c - m_use, -100.0f)) - 7;
+  psc[0] = (lh ? X[1] : X[0]) + 127;
+  psc[1] = (lh ? X[3] : X[2]) + 127;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const float mX = m_use + (float)X[kb];   // integral: p / 2^X exactly
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[kb][i] = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -mX));
+  }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "qk4v8_split.h"
+
 namespace qk4v8 {
 
 constexpr int kKvTile = 128;    // keys per attention KV tile
@@ -60,9 +62,9 @@ struct DecodeParams {
   float softmax_scale;
   uint8_t* ws;
 };
-// Keys the split range of one sequence covers at most (kv_len, or less with a window).
-int decode_key_span(int kv_len, int q_len, int window);
 // Splits of the KV range per (batch, kv-head); rows = (q_heads / kv_heads) * q_len.
+// With requested == 0 the count comes from the current device's CU count and
+// the split kernel's occupancy; 0 when that query fails.
 int decode_num_splits(int batch, int kv_heads, int rows, int head_dim, int span, int requested);
 size_t decode_workspace_bytes(int batch, int q_len, int q_heads, int kv_heads, int head_dim, int splits);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);

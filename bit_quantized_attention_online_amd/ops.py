@@ -93,8 +93,9 @@ def lib():
             getattr(L, fn).argtypes = [ctypes.POINTER(PrefillArgs), ctypes.c_void_p]
         L.qk4v8_decode_workspace_bytes.restype = ctypes.c_size_t
         L.qk4v8_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
-        L.qk4v8_attn_decode.restype = ctypes.c_int
-        L.qk4v8_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+        for fn in ("qk4v8_attn_decode",):
+            getattr(L, fn).restype = ctypes.c_int
+            getattr(L, fn).argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
         L.qk4v8_kv_append.restype = ctypes.c_int
         L.qk4v8_kv_append.argtypes = [ctypes.POINTER(AppendArgs), ctypes.c_void_p]
         _lib = L

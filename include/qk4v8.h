@@ -35,8 +35,11 @@
  * Conventions for every call:
  *   - All data pointers are DEVICE pointers; the caller owns every buffer,
  *     including the workspace sized by the *_workspace_bytes queries.  The
- *     library allocates no device memory and keeps no state between calls
- *     (nothing is calibrated or cached).
+ *     library allocates no device memory and keeps no data between calls
+ *     (nothing is calibrated).  Its only state is per device ordinal and
+ *     read-only once set: whether the device is a gfx950, the CU count times
+ *     the decode kernels' occupancy (which sizes decode's automatic split
+ *     count).
  *   - Work is enqueued on `stream` and is asynchronous; the library never
  *     synchronizes the host.
  *   - Arguments are validated on the host before any launch; a failed check
@@ -59,7 +62,7 @@
 extern "C" {
 #endif
 
-#define QK4V8_ABI_VERSION 6
+#define QK4V8_ABI_VERSION 7
 
 typedef enum {
   QK4V8_OK = 0,
@@ -134,11 +137,12 @@ qk4v8_status qk4v8_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int3
  *               the accuracy of exact attention on the quantized operands to
  *               about 2e-3 relative L2.
  *               1 (fast mode): one E4M3 term per weight, an integral running
- *               maximum (every rescale an exact power of two) and the same
- *               range exponent; half the P·V matrix work and fewer vector
+ *               maximum (every rescale an exact power of two) and one E8M0
+ *               range exponent per query row and aligned 32-key block (the
+ *               MX block size); half the P·V matrix work and fewer vector
  *               instructions, at about 2e-2 relative L2 from exact attention.
  *               Its result is independent of the tiling: with base-2 scores
- *               t = s*log2(e) and 128-key blocks B aligned at multiples of 128,
+ *               t = s*log2(e) and 32-key blocks B aligned at multiples of 32,
  *               p~_j = 2^X_B * E4M3(2^(t_j - X_B)), X_B = floor(max_B t) - 7, and
  *               o = sum_j p~_j v_j / sum_j p~_j.
  *   hadamard  : 1 rotates every Q and K row by the Sylvester-Hadamard matrix
@@ -211,12 +215,20 @@ qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t 
  *   kv_lens  : device int32 [batch] with q_len <= kv_lens[b] <= kv_len, or NULL
  *              for every sequence having kv_len entries.  Cache rows at or
  *              past a sequence's length are never read (their bytes, and the
- *              V scales of tiles that start there, may be anything).
+ *              V scales of tiles that start there, may be anything).  A
+ *              length outside that range is outside the contract and is read
+ *              on the device as follows: above kv_len it is taken as kv_len
+ *              (no read past the capacity or the block-table row), below
+ *              q_len the sequence is empty (zero output rows, lse -inf).
  *   o        : out bf16 [batch, q_len, q_heads, head_dim], strides o_stride
  *   lse      : out fp32 [batch, q_len, q_heads] contiguous, natural log; may be NULL.
  *   head_dim ∈ {64, 128}; v_tile_rows ∈ {32, 64, 128, 256};
  *   1 <= q_len <= kv_len <= cap; (q_heads / kv_heads) * q_len <= 64.
- *   num_splits: KV splits per (batch, kv-head), 0 = chosen by the library.
+ *   num_splits: KV splits per (batch, kv-head), 0 = chosen by the library
+ *              from the current device (one round of resident workgroups:
+ *              CU count times the split kernel's occupancy, at least 8
+ *              tiles of 128 keys per split); with 0 the workspace query and
+ *              the call return 0 / QK4V8_ERR_HIP when no device answers.
  *   workspace : at least qk4v8_decode_workspace_bytes() bytes, 256-byte aligned
  *               (fp32 partial outputs and log-sum-exps of the splits; with a
  *               single split and an 8-byte aligned o whose strides are

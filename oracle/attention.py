@@ -157,9 +157,10 @@ def qk4v8_decode(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens, v_tile_r
 #
 # P·V on FP8 (E4M3) with one term per probability.  Its definition does not
 # depend on how keys are tiled: with base-2 scores t_ij = s_ij * log2(e), the
-# keys of a row are grouped in blocks of 128 (key indices [128a, 128a + 128)),
-# each block gets the range exponent X = floor(max_j t_ij) - 7 over its visible
-# keys, and each weight is rounded to E4M3 on that range:
+# keys of a row are grouped in aligned blocks of 32 (key indices [32a, 32a +
+# 32), the MX block size of the MiMo page's section "MXFP4专家量化"), each block
+# gets the range exponent X = floor(max_j t_ij) - 7 over its visible keys (an
+# E8M0 scale, as in MX), and each weight is rounded to E4M3 on that range:
 #     p~_ij = 2^X * E4M3_RNE(2^(t_ij - X))       (2^(t - X) < 256, no saturation)
 #     o_i   = sum_j p~_ij v_j / sum_j p~_ij,   lse_i = ln(sum_j p~_ij)
 # A common factor 2^M per row (M any integer) cancels in o and is added back
@@ -167,7 +168,7 @@ def qk4v8_decode(q_bits, k_codes, k_scales, v_codes, v_scales, kv_lens, v_tile_r
 # detail below the gate and is not modelled here (see ``attention``).
 # ---------------------------------------------------------------------------
 
-FAST_P_BLOCK = 128
+FAST_P_BLOCK = 32
 FAST_P_HEADROOM = 7
 _LOG2E = 1.4426950408889634
 

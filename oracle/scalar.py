@@ -99,7 +99,7 @@ def attention_rows(q, k, v, sigma, causal):
     return out, lses
 
 
-def attention_rows_fast_p(q, k, v, sigma, causal, block=128, headroom=7):
+def attention_rows_fast_p(q, k, v, sigma, causal, block=32, headroom=7):
     """Single-term E4M3 probabilities by loops: base-2 scores t = s*log2(e),
     keys in blocks [block*a, block*a + block), each block's range exponent
     X = floor(max t) - headroom (floor found by stepping), each weight rounded

@@ -142,6 +142,20 @@ def test_decode_workloads_full_size_sampled(gpu, cfg):
         ro, _ = oatt.qk4v8_decode(q[b:b + 1], rkc[None], rks[None], rvc[None], rvs[None],
                                   np.array([w["kv_len"]]), w["v_tile_rows"], 1 / math.sqrt(w["d"]), window=1024)
         assert_attn_close(ow[b:b + 1], ro, f"workload {cfg} window 1024 batch {b}")
+    if cfg == 3:
+        # the same cache as 256-token pages in a shuffled order (the paged
+        # launch the bench times): the same bits as the contiguous cache, so
+        # the sampled batches above also pin the paged result to the oracle
+        from tests.test_gpu_paged import _table, _to_pages
+        P, R = 256, w["v_tile_rows"]
+        table = _table(w["B"], w["kv_len"] // P, 0, seed=w["kv_len"])
+        pages = (_to_pages(kc, table, P, P), _to_pages(ks, table, P, P), _to_pages(vc, table, P, P),
+                 _to_pages(vs, table, P, P // R))
+        del kc, ks, vc, vs
+        op = ops.attn_decode(to_dev(q), *pages, w["kv_len"], v_tile_rows=R,
+                             block_table=torch.from_numpy(table).cuda(), page_size=P)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev_bf16(op), o), "paged decode differs from the contiguous cache"
 
 
 @pytest.mark.parametrize("q_len,d", [(1, 128), (4, 128), (2, 64)])
@@ -233,3 +247,71 @@ def test_decode_ignores_cache_bytes_past_each_length(gpu, q_len, d, R):
     ro, _ = oatt.qk4v8_decode(q, rkc, rks, rvc.reshape(B, Hkv, cap, d), rvs.reshape(B, Hkv, -1), lens, R,
                               1 / math.sqrt(d))
     assert_attn_close(out, ro, "decode past-length NaN bytes")
+
+
+@pytest.mark.parametrize("splits,paged", [(0, False), (3, False), (1, False), (2, True)])
+def test_decode_out_of_contract_lengths_stay_in_bounds(gpu, splits, paged):
+    """kv_lens above kv_len are read as kv_len, below q_len as an empty
+    sequence (zero rows, lse -inf).  The cache bytes past kv_len are E4M3 NaN
+    patterns, and cap is larger than every length, so a read past kv_len
+    would show as NaN in the output while staying inside the allocation."""
+    from bit_quantized_attention_online_amd import ops
+    B, Hq, Hkv, q_len, kv_len, cap, d, R = 4, 8, 2, 4, 600, 1024, 128, 256
+    lens = np.array([900, 0, 3, 450], dtype=np.int32)
+    clamped = np.array([600, 0, 0, 450])
+    rng = np.random.default_rng(77)
+    k = synth.bf16_bits(rng.standard_normal((B, Hkv, cap, d)).astype(np.float32))
+    v = synth.bf16_bits(rng.standard_normal((B, Hkv, cap, d)).astype(np.float32))
+    q = synth.bf16_bits(rng.standard_normal((B, q_len, Hq, d)).astype(np.float32))
+    print(f"[case] decode out-of-contract lengths {lens.tolist()} splits={splits} paged={paged}", flush=True)
+    rkc, rks = quant.quantize_qk(k)
+    rvc, rvs = quant.quantize_v(v.reshape(B * Hkv, cap, d), R)
+    rvc, rvs = rvc.reshape(B, Hkv, cap, d), rvs.reshape(B, Hkv, -1)
+    kc, ks, vc, vs = (rkc.copy(), rks.copy(), rvc.copy(), rvs.copy())
+    kc[:, :, kv_len:] = 0xFF
+    ks[:, :, kv_len:] = 0xFF
+    vc[:, :, kv_len:] = 0x7F                      # E4M3 NaN
+    vs[:, :, -(-kv_len // R):] = 0xFF             # E8M0 NaN
+    dev = torch.device("cuda:0")
+    cache = [torch.from_numpy(x).to(dev) for x in (kc, ks, vc, vs)]
+    kw = {}
+    if paged:
+        P = 256
+        npp = cap // P
+        table = np.arange(B * npp, dtype=np.int32)[::-1].copy().reshape(B, npp)
+
+        def pages(t, per):
+            src = t.reshape((B, Hkv, npp, per) + tuple(t.shape[3:])).transpose(1, 2)
+            pool = torch.empty((B * npp, Hkv, per) + tuple(t.shape[3:]), dtype=t.dtype, device=dev)
+            pool[torch.from_numpy(table.reshape(-1)).long().to(dev)] = src.reshape((B * npp, Hkv, per)
+                                                                                  + tuple(t.shape[3:]))
+            return pool
+
+        cache = [pages(cache[0], P), pages(cache[1], P), pages(cache[2], P), pages(cache[3], P // R)]
+        kw = dict(block_table=torch.from_numpy(table).to(dev), page_size=P)
+    o, l = ops.attn_decode(to_dev(q), *cache, kv_len, v_tile_rows=R, kv_lens=torch.from_numpy(lens).to(dev),
+                           num_splits=splits, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    o, l = from_dev_bf16(o), l.cpu().numpy()
+    assert np.isfinite(o).all()
+    live = clamped > 0
+    ro, rl = oatt.qk4v8_decode(q[live], rkc[live], rks[live], rvc[live], rvs[live], clamped[live], R,
+                               1 / math.sqrt(d))
+    assert_attn_close(o[live], ro, "clamped lengths")
+    assert np.abs(l[live] - rl).max() < 5e-3
+    assert (o[~live] == 0).all() and np.isneginf(l[~live]).all()
+
+
+def test_decode_auto_split_count_on_mi355x(gpu):
+    """num_splits = 0 derives the count from the CU count and the split
+    kernel's occupancy; on MI355X (256 CUs) that gives 2 splits for the
+    decode workload and 3 for block verify."""
+    from bit_quantized_attention_online_amd import ops
+    for cfg, want in ((3, 2), (5, 3)):
+        w = synth.WORKLOADS[cfg]
+        q = torch.empty((w["B"], w["q_len"], w["Hq"], w["d"]), dtype=torch.bfloat16, device="cuda")
+        kc = torch.empty((w["B"], w["Hkv"], w["kv_len"], w["d"] // 2), dtype=torch.uint8, device="cuda")
+        auto = ops.decode_workspace_bytes(q, kc, w["kv_len"], w["v_tile_rows"])
+        forced = ops.decode_workspace_bytes(q, kc, w["kv_len"], w["v_tile_rows"], num_splits=want)
+        print(f"[case] auto splits {w['name']}: {auto} vs {forced} bytes", flush=True)
+        assert auto == forced > 0

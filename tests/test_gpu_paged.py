@@ -58,6 +58,12 @@ def test_paged_decode_equals_contiguous(gpu, B, Hq, Hkv, q_len, d, R, P, npp, ra
     kc, ks = ops.quantize_qk(to_dev(k))
     vc, vs = ops.quantize_v(to_dev(v).reshape(B * Hkv, cap, d), R)
     vc, vs = vc.reshape(B, Hkv, cap, d), vs.reshape(B, Hkv, -1)
+    # the cache codes are the oracle's own quantization, bit for bit
+    rkc, rks = quant.quantize_qk(k)
+    rvc, rvs = quant.quantize_v(v.reshape(B * Hkv, cap, d), R)
+    rvc, rvs = rvc.reshape(B, Hkv, cap, d), rvs.reshape(B, Hkv, -1)
+    assert np.array_equal(kc.cpu().numpy(), rkc) and np.array_equal(ks.cpu().numpy(), rks)
+    assert np.array_equal(vc.cpu().numpy(), rvc) and np.array_equal(vs.cpu().numpy(), rvs)
     table = _table(B, npp, 5, seed=cap)
     pk, pks, pv = _to_pages(kc, table, P, P), _to_pages(ks, table, P, P), _to_pages(vc, table, P, P)
     pvs = _to_pages(vs, table, P, P // R)
@@ -69,10 +75,13 @@ def test_paged_decode_equals_contiguous(gpu, B, Hq, Hkv, q_len, d, R, P, npp, ra
                              block_table=bt, page_size=P)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    # the oracle on the cache the pages stand for
+    # the pages gather back into the oracle's cache, and the oracle on its
+    # own codes gives the reference
     g = [ocache.gather_pages(t.cpu().numpy(), table, P) for t in (pk, pks, pv)]
     gvs = ocache.gather_pages(pvs.cpu().numpy(), table, P, rows_per_page=P // R)
-    ro, rl = oatt.qk4v8_decode(q, g[0], g[1], g[2], gvs, lens, R, 1 / math.sqrt(d), window=W)
+    assert np.array_equal(g[0], rkc) and np.array_equal(g[1], rks) and np.array_equal(g[2], rvc)
+    assert np.array_equal(gvs, rvs)
+    ro, rl = oatt.qk4v8_decode(q, rkc, rks, rvc, rvs, lens, R, 1 / math.sqrt(d), window=W)
     assert_attn_close(from_dev_bf16(o2), ro, "paged decode")
     assert np.abs(l2.cpu().numpy() - rl).max() < 5e-3
 

@@ -48,23 +48,32 @@ def test_constant_v_and_within_block_permutation():
     v = np.tile(rng.standard_normal(d), (nk, 1))[None, None]
     o, _ = A.attention_fast_p(q, k, v, 0.3, False)
     assert np.allclose(o, v[:, :, :3], rtol=0, atol=1e-12)
-    # permuting keys inside each 128-key block leaves the result unchanged
+    # permuting keys inside each aligned 32-key block leaves the result unchanged
     v = rng.standard_normal((1, 1, nk, d))
-    perm = np.concatenate([rng.permutation(128), 128 + rng.permutation(128)])
+    perm = np.concatenate([32 * b + rng.permutation(32) for b in range(nk // 32)])
     o1, l1 = A.attention_fast_p(q, k, v, 0.3, False)
     o2, l2 = A.attention_fast_p(q, k[:, :, perm], v[:, :, perm], 0.3, False)
     assert np.allclose(o1, o2, rtol=0, atol=1e-12) and np.allclose(l1, l2, rtol=0, atol=1e-12)
 
 
-def test_error_bound_against_exact():
-    # every weight carries a relative rounding error of at most 2^-4 (E4M3 has
-    # 3 mantissa bits) unless it is below the block's subnormal range; so the
-    # output moves by at most about 2 * 2^-4 * max|v|
-    rng = np.random.default_rng(3)
-    q = rng.standard_normal((1, 2, 64, 32))
-    k = rng.standard_normal((1, 2, 400, 32))
-    v = rng.standard_normal((1, 2, 400, 32))
-    o, _ = A.attention_fast_p(q, k, v, 0.2, True)
-    ro, _ = A.attention(q, k, v, 0.2, True)
-    assert np.abs(o - ro).max() <= 2 * 2.0 ** -4 * np.abs(v).max()
-    assert np.abs(o - ro).max() > 0          # the rounding is really applied
+def test_range_exponent_is_per_32_key_block():
+    # two 32-key blocks whose base-2 scores are 0 and -15.3: with one range
+    # exponent per 32 keys the small block's weights keep 3 mantissa bits
+    # (X = floor(-15.3) - 7 = -23, 2^(-15.3 + 23) = 207.9 -> E4M3 208), while a
+    # range shared with the large block (X = -7) would put them in E4M3's
+    # subnormals, 2^-8.3 -> 2 * 2^-9, an error of 23%.  Hand-worked values.
+    from oracle.formats import e4m3_decode, e4m3_encode
+    nk = 64
+    k = np.zeros((nk, 2))
+    k[32:, 0] = -15.3
+    q = np.array([[math.log(2.0), 0.0]])   # t = s * log2(e) = k[:, 0]
+    v = np.zeros((nk, 2))
+    v[:32, 0] = 1.0
+    v[32:, 1] = 1.0
+    o, _ = A.attention_fast_p(q[None, None], k[None, None], v[None, None], 1.0, False)
+    w1q = float(e4m3_decode(e4m3_encode(np.array([2.0 ** (-15.3 + 23)])))[0]) * 2.0 ** -23
+    assert w1q == 208 * 2.0 ** -23
+    want = np.array([32.0, 32 * w1q]) / (32 + 32 * w1q)
+    assert np.allclose(o[0, 0, 0], want, rtol=0, atol=1e-15)
+    shared = 2 * 2.0 ** -9 * 2.0 ** -7        # the same weight on a 64-key shared range
+    assert abs(shared / 2.0 ** -15.3 - 1) > 0.2 and abs(w1q / 2.0 ** -15.3 - 1) <= 2.0 ** -4
