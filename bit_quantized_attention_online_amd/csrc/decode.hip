@@ -491,4 +491,40 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   return p.head_dim == 64 ? launch_decode_d<64>(p, stream) : launch_decode_d<128>(p, stream);
 }
 
+// Split partials of the allocation-free decode entry point.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: the kernels get
+// the device address that hipGetSymbolAddress returns for the current device,
+// looked up on the first call on each device and kept per device ordinal.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static hipError_t scratch_address(uint8_t** out) {
+  static std::atomic<uint8_t*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uint8_t* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* sym = nullptr;
+    e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    p = static_cast<uint8_t*>(sym);
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_decode_noalloc(DecodeParams p, size_t need, hipStream_t stream) {
+  if (need > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  uint8_t* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  // every split writes all of its partial rows before the merge reads them,
+  // so nothing in the array needs clearing between calls
+  p.ws = ws;
+  return launch_decode(p, stream);
+}
+
 }  // namespace qk4v8

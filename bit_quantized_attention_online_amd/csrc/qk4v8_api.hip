@@ -106,8 +106,10 @@ int decode_splits(const qk4v8_decode_args* a) {
                            decode_key_span(a->kv_len, a->q_len, a->window), a->num_splits);
 }
 
-// Buffers of a decode call; *need receives the split partials' bytes.
-qk4v8_status validate_decode_memory(const qk4v8_decode_args* a, size_t* need) {
+// Buffers of a decode call.  `caller_ws`: the partials go to the caller's
+// workspace (checked here); otherwise to the library's fixed array, whose
+// size bounds the call.  *need receives the partials' bytes.
+qk4v8_status validate_decode_memory(const qk4v8_decode_args* a, bool caller_ws, size_t* need) {
   if (!a->q || !a->k_codes || !a->k_scales || !a->v_codes || !a->v_scales || !a->o) return QK4V8_ERR_NULL;
   for (int i = 0; i < 3; ++i)
     if (a->q_stride[i] < 0 || a->q_stride[i] % 8 != 0 || a->o_stride[i] < 0) return QK4V8_ERR_STRIDE;
@@ -121,8 +123,12 @@ qk4v8_status validate_decode_memory(const qk4v8_decode_args* a, size_t* need) {
   const int splits = decode_splits(a);
   if (splits < 1) return QK4V8_ERR_HIP;   // the device's occupancy query failed
   *need = decode_workspace_bytes(a->batch, a->q_len, a->q_heads, a->kv_heads, a->head_dim, splits);
-  if (a->workspace == nullptr || !aligned(a->workspace, kWsAlign)) return QK4V8_ERR_WORKSPACE;
-  if (a->workspace_bytes < *need) return QK4V8_ERR_WORKSPACE;
+  if (caller_ws) {
+    if (a->workspace == nullptr || !aligned(a->workspace, kWsAlign)) return QK4V8_ERR_WORKSPACE;
+    if (a->workspace_bytes < *need) return QK4V8_ERR_WORKSPACE;
+  } else if (*need > kNoAllocScratchBytes) {
+    return QK4V8_ERR_WORKSPACE;
+  }
   return QK4V8_OK;
 }
 
@@ -182,12 +188,14 @@ size_t qk4v8_prefill_workspace_bytes(const qk4v8_prefill_args* a) {
 
 namespace {
 
-qk4v8_status run_decode(const qk4v8_decode_args* a, hipStream_t stream) {
+// A decode call; caller_ws false: the partials live in the library's fixed
+// per-device array (qk4v8_attn_decode_noalloc), nothing is allocated.
+qk4v8_status run_decode(const qk4v8_decode_args* a, hipStream_t stream, bool caller_ws) {
   qk4v8_status st = validate_decode(a);
   if (st != QK4V8_OK) return st;
   if (a->batch == 0) return QK4V8_OK;
   size_t need = 0;
-  st = validate_decode_memory(a, &need);
+  st = validate_decode_memory(a, caller_ws, &need);
   if (st != QK4V8_OK) return st;
   st = check_device();
   if (st != QK4V8_OK) return st;
@@ -202,7 +210,7 @@ qk4v8_status run_decode(const qk4v8_decode_args* a, hipStream_t stream) {
   p.window = a->window;
   p.block_table = a->block_table; p.page_size = a->page_size; p.pages_per_seq = a->pages_per_seq;
   p.ws = static_cast<uint8_t*>(a->workspace);
-  return from_hip(launch_decode(p, stream));
+  return from_hip(caller_ws ? launch_decode(p, stream) : launch_decode_noalloc(p, need, stream));
 }
 
 enum PrefillPart { kPack = 1, kAttn = 2 };
@@ -296,7 +304,11 @@ qk4v8_status qk4v8_kv_append(const qk4v8_append_args* a, hipStream_t stream) {
 }
 
 qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream) {
-  return run_decode(a, stream);
+  return run_decode(a, stream, true);
+}
+
+qk4v8_status qk4v8_attn_decode_noalloc(const qk4v8_decode_args* a, hipStream_t stream) {
+  return run_decode(a, stream, false);
 }
 
 }  // extern "C"

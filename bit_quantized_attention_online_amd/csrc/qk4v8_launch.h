@@ -68,6 +68,10 @@ struct DecodeParams {
 int decode_num_splits(int batch, int kv_heads, int rows, int head_dim, int span, int requested);
 size_t decode_workspace_bytes(int batch, int q_len, int q_heads, int kv_heads, int head_dim, int splits);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// The same launch with the split partials in the library's fixed per-device
+// array instead of p.ws (no allocation); `need` bytes must fit it.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t launch_decode_noalloc(DecodeParams p, size_t need, hipStream_t stream);
 
 // KV-cache append: new K rows to MXFP4 and V rows to per-tile FP8 in the
 // decode cache layout (see append.hip).

@@ -21,7 +21,11 @@ STATUS_NAMES = {0: "QK4V8_OK", 1: "QK4V8_ERR_NULL", 2: "QK4V8_ERR_SHAPE", 3: "QK
 EXPORTED = ["qk4v8_abi_version", "qk4v8_status_string", "qk4v8_quantize_qk", "qk4v8_quantize_v",
             "qk4v8_prefill_workspace_bytes", "qk4v8_attn_prefill", "qk4v8_prefill_pack_kv",
             "qk4v8_attn_prefill_packed", "qk4v8_decode_workspace_bytes", "qk4v8_attn_decode",
-            "qk4v8_kv_append"]
+            "qk4v8_attn_decode_noalloc", "qk4v8_kv_append"]
+
+# Size of the fixed per-GPU array qk4v8_attn_decode_noalloc keeps its split
+# partials in (QK4V8_NOALLOC_SCRATCH_BYTES of include/qk4v8.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class PrefillArgs(ctypes.Structure):
@@ -93,7 +97,7 @@ def lib():
             getattr(L, fn).argtypes = [ctypes.POINTER(PrefillArgs), ctypes.c_void_p]
         L.qk4v8_decode_workspace_bytes.restype = ctypes.c_size_t
         L.qk4v8_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
-        for fn in ("qk4v8_attn_decode",):
+        for fn in ("qk4v8_attn_decode", "qk4v8_attn_decode_noalloc"):
             getattr(L, fn).restype = ctypes.c_int
             getattr(L, fn).argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
         L.qk4v8_kv_append.restype = ctypes.c_int
@@ -296,6 +300,24 @@ def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256
     a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _check(lib().qk4v8_attn_decode(ctypes.byref(a), _stream(stream)), "qk4v8_attn_decode")
     return (o, lse) if return_lse else o
+
+
+def attn_decode_noalloc(q, k_codes, k_scales, v_codes, v_scales, kv_len, out, lse=None, v_tile_rows=256,
+                        kv_lens=None, num_splits=0, softmax_scale=None, stream=None, hadamard=False, window=0,
+                        block_table=None, page_size=0):
+    """``attn_decode`` through qk4v8_attn_decode_noalloc: the caller passes the
+    output (and optionally an fp32 lse [B, q_len, Hq]) and the library keeps
+    the split partials in its fixed per-GPU array, allocating nothing.  Calls
+    that overlap on one GPU race (they share the array)."""
+    _bits16(q)
+    if kv_lens is not None and kv_lens.dtype != torch.int32:
+        raise TypeError("kv_lens must be int32")
+    a = _decode_args(q, k_codes, k_scales, v_codes, v_scales, out, lse, kv_len, v_tile_rows, kv_lens, num_splits,
+                     softmax_scale, block_table, page_size)
+    a.hadamard = int(bool(hadamard))
+    a.window = window
+    _check(lib().qk4v8_attn_decode_noalloc(ctypes.byref(a), _stream(stream)), "qk4v8_attn_decode_noalloc")
+    return out
 
 
 def kv_append(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows=256,

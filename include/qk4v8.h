@@ -39,7 +39,8 @@
  *     (nothing is calibrated).  Its only state is per device ordinal and
  *     read-only once set: whether the device is a gfx950, the CU count times
  *     the decode kernels' occupancy (which sizes decode's automatic split
- *     count).
+ *     count), and the address of the fixed array of
+ *     qk4v8_attn_decode_noalloc.
  *   - Work is enqueued on `stream` and is asynchronous; the library never
  *     synchronizes the host.
  *   - Arguments are validated on the host before any launch; a failed check
@@ -282,6 +283,23 @@ typedef struct {
 /* Workspace bytes qk4v8_attn_decode needs for these sizes (0 on bad sizes). */
 size_t qk4v8_decode_workspace_bytes(const qk4v8_decode_args* a);
 qk4v8_status qk4v8_attn_decode(const qk4v8_decode_args* a, hipStream_t stream);
+
+/*
+ * qk4v8_attn_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  `workspace` and `workspace_bytes` are
+ * ignored; the split partials go to a fixed device array of
+ * QK4V8_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The call allocates nothing and otherwise behaves
+ * as qk4v8_attn_decode: the same arguments, validation, kernels and result
+ * bits.  QK4V8_ERR_WORKSPACE when the partials (the bytes
+ * qk4v8_decode_workspace_bytes reports) exceed the array; pass a smaller
+ * num_splits then.  Calls on one GPU share its array and it keeps the last
+ * call's partials: calls that overlap in time on one GPU (on different
+ * streams, or from several host threads) race and may return wrong results.
+ */
+#define QK4V8_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+qk4v8_status qk4v8_attn_decode_noalloc(const qk4v8_decode_args* a, hipStream_t stream);
 
 /*
  * KV-cache append (MpFA page §6.1: the cache is kept quantized, so new tokens

@@ -148,6 +148,24 @@ def test_decode_auto_splits_need_a_device():
     assert L.qk4v8_attn_decode(ctypes.byref(_decode()), None) == 6
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_len=9), 2), (dict(kv_len=1025), 2), (dict(v_codes=None), 1), (dict(k_codes=4104), 3),
+    (dict(workspace=None, workspace_bytes=0, num_splits=2, batch=0), 0),          # empty: no-op, no workspace
+    # partials beyond the fixed array (64 x 8 x 8 splits x 64 rows x 516 B = 135 MB > 32 MiB)
+    (dict(batch=64, q_len=8, kv_len=32768, cap=32768, num_splits=8), 5),
+])
+def test_decode_noalloc_validation(kw, status):
+    a = _decode(**kw)
+    a.workspace, a.workspace_bytes = None, 0     # ignored by this entry point
+    assert ops.lib().qk4v8_attn_decode_noalloc(ctypes.byref(a), None) == status
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "qk4v8.h")).read()
+    m = re.search(r"#define QK4V8_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == ops.NOALLOC_SCRATCH_BYTES
+
+
 def test_append_paging_validation():
     L = ops.lib()
     assert L.qk4v8_kv_append(ctypes.byref(_append(block_table=4096, page_size=200, pages_per_seq=5,
