@@ -1,17 +1,21 @@
 #!/usr/bin/env python3
 """Throughput of the QK4V8 hot path on one MI355X, printed as ONE JSON line.
 
-Step = one full prefill of the causal GQA workload (batch 4, 32 query / 8 KV
-heads, 4096 tokens, head_dim 128, 4 outlier K channels x20): the K/V quantize
-pre-pass plus the attention kernel, which quantizes Q in its prologue.  The
-decode (batch 64, 64/8 heads, 32768 cached tokens) and block-verify (batch 32,
-8 queries over 16384 + 8 cached tokens) workloads are timed in the same run and
-reported as extra objects, and so is the 131072-token causal prefill (batch 1,
-64 query / 8 KV heads, 2% of K rows x10).  Inputs are seeded and synthetic and resident in HBM
-before timing starts; each workload first runs untimed for half a second so
-that the GPU's clocks settle, then W warmup steps, then K timed steps.
+Step = one full prefill of the long-context causal workload (batch 1, 64 query
+/ 8 KV heads, 131072 tokens, head_dim 128, 2% of K rows x10): the K/V quantize
+pre-pass plus the attention kernel, which quantizes Q in its prologue.  That
+is the largest configuration one GPU holds, and `value` is its whole-step
+throughput.  The causal GQA prefill (batch 4, 32 query / 8 KV heads, 4096
+tokens, 4 outlier K channels x20), the decode (batch 64, 64/8 heads, 32768
+cached tokens) and block-verify (batch 32, 8 queries over 16384 + 8 cached
+tokens) workloads, the cache writer and the standalone quantizers are timed in
+the same run and reported as extra objects.  Inputs are seeded and synthetic
+and resident in HBM before timing starts; each workload first runs untimed for
+half a second so that the GPU's clocks settle, then W warmup steps, then K
+timed steps (at least 50 for the sub-millisecond workloads).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--peaks] [--only PARTS]
 """
 
 import argparse
@@ -31,8 +35,25 @@ PEAK_FP8_TFLOPS = 5000.0       # dense FP8 MFMA
 # QK^T runs on FP4 and P·V on FP8 with equal algorithmic flops, so the time
 # floor is F/2/P_fp4 + F/2/P_fp8, i.e. the harmonic mean of the two peaks.
 PEAK_MIXED_TFLOPS = 2.0 / (1.0 / PEAK_FP4_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
+PEAK_BF16_TFLOPS = 2500.0      # dense BF16 MFMA
+# bf16 probabilities: P·V runs on the bf16 matrix core, so that path's floor is
+# F/2/P_fp4 + F/2/P_bf16
+PEAK_MIXED_BF16_TFLOPS = 2.0 / (1.0 / PEAK_FP4_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
+
+
+def mode_peak(p_mode):
+    """The mixed roofline of a probability format: FP4 QK^T plus P·V on the
+    matrix core of the format's own dtype."""
+    from bit_quantized_attention_online_amd import ops
+    m = ops.P_DEFAULT_MODE if p_mode == ops.P_DEFAULT else p_mode
+    return PEAK_MIXED_BF16_TFLOPS if m == ops.P_BF16 else PEAK_MIXED_TFLOPS
+
+
+MODE_DTYPE = {1: "mxfp4xmxfp4+fp8xfp8->fp32", 2: "mxfp4xmxfp4+fp8xfp8->fp32",
+              3: "mxfp4xmxfp4+bf16xbf16->fp32"}
 SETTLE_S = 0.5                 # untimed sustained load before the warmup steps
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_causal_gqa_n4096_traffic.json")
+LONG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_long_causal_n131072_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "bit_quantized_attention_online_amd", "csrc", "prefill.hip")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.json")
 DECODE_SOURCE = os.path.join(ROOT, "bit_quantized_attention_online_amd", "csrc", "decode.hip")
@@ -97,7 +118,10 @@ def settle(torch, step, seconds=SETTLE_S):
         torch.cuda.synchronize()
 
 
-def bench_prefill(torch, ops, synth, steps, warmup):
+def bench_prefill(torch, ops, synth, steps, warmup, keep=None):
+    """The causal GQA prefill (batch 4, 32/8 heads, 4096 tokens): the default
+    step, fast mode, the Hadamard-rotated step and the 1024-key window.  With
+    ``keep`` a dict, the device K and V are left in it for the quantizer bench."""
     w = synth.WORKLOADS[2]
     log("[bench] generating the causal GQA prefill workload")
     q, k, v = synth.prefill_inputs(2)
@@ -129,9 +153,29 @@ def bench_prefill(torch, ops, synth, steps, warmup):
     assert torch.isfinite(pp.o.float()).all().item(), "non-finite prefill output"
     pairs = w["B"] * w["Hq"] * causal_pairs(w["Nq"], w["Nk"])
     flops = pairs * 4.0 * w["d"]
+    modes = {}
+    for name, pm in (("fp8_two_term", ops.P_FP8_TWO_TERM), ("bf16", ops.P_BF16)):
+        ppm = ops.PackedPrefill(qd, kd, vd, causal=True, softmax_scale=1.0 / math.sqrt(w["d"]),
+                                v_tile_rows=w["v_tile_rows"], p_mode=pm)
+        settle(torch, lambda: (ppm.pack(), ppm.attend()), seconds=0.2)
+        for _ in range(warmup):
+            ppm.pack()
+            ppm.attend()
+        evm = [Events(torch, 3) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in evm:
+            e.record(0, stream)
+            ppm.pack(stream)
+            e.record(1, stream)
+            ppm.attend(stream)
+            e.record(2, stream)
+        torch.cuda.synchronize()
+        modes[name] = dict(pack_ms=sum(e.ms(0, 1) for e in evm) / steps, attn_ms=sum(e.ms(1, 2) for e in evm) / steps)
+        assert torch.isfinite(ppm.o.float()).all().item(), f"non-finite {name} output"
+        del ppm
     # fast mode (single-term FP8 probabilities) on the same inputs
     ppf = ops.PackedPrefill(qd, kd, vd, causal=True, softmax_scale=1.0 / math.sqrt(w["d"]),
-                            v_tile_rows=w["v_tile_rows"], p_terms=1)
+                            v_tile_rows=w["v_tile_rows"], p_mode=1)
     ppf.pack()
     settle(torch, ppf.attend, seconds=0.2)
     for _ in range(warmup):
@@ -184,14 +228,16 @@ def bench_prefill(torch, ops, synth, steps, warmup):
     assert torch.isfinite(ppw.o.float()).all().item(), "non-finite windowed output"
     swa_flops = w["B"] * w["Hq"] * causal_pairs(w["Nq"], w["Nk"], SWA_WINDOW) * 4.0 * w["d"]
     del ppw
+    if keep is not None:
+        keep.update(k=kd, v=vd)
     return dict(w=w, wall_ms=wall * 1e3 / steps, pack_ms=pack_ms, attn_ms=attn_ms, flops=flops, pairs=pairs,
-                fast_ms=fast_ms, had=had, swa=dict(ms=swa_ms, flops=swa_flops))
+                fast_ms=fast_ms, had=had, swa=dict(ms=swa_ms, flops=swa_flops), modes=modes)
 
 
 def bench_prefill_long(torch, ops, synth, steps, warmup):
-    """The 131072-token causal prefill (batch 1, 64 query / 8 KV heads,
-    head_dim 128, 2% of K rows x10), drawn on the GPU with torch's seeded
-    generator; pack + attention per step, the attention timed separately."""
+    """The headline step: the 131072-token causal prefill (batch 1, 64 query /
+    8 KV heads, head_dim 128, 2% of K rows x10), drawn on the GPU with torch's
+    seeded generator; pack + attention per step, each timed by events."""
     w = synth.WORKLOADS[4]
     B, Hq, Hkv, N, d = w["B"], w["Hq"], w["Hkv"], w["Nq"], w["d"]
     dev = torch.device("cuda:0")
@@ -203,15 +249,18 @@ def bench_prefill_long(torch, ops, synth, steps, warmup):
     rows = torch.rand((B, Hkv, N, 1), generator=g, device=dev) < w["k_outlier_row_frac"]
     k = torch.where(rows, k * w["k_outlier_factor"], k).to(torch.bfloat16)
     v = torch.randn((B, Hkv, N, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    del rows
     pp = ops.PackedPrefill(q, k, v, causal=True, softmax_scale=1.0 / math.sqrt(d), v_tile_rows=w["v_tile_rows"])
     stream = torch.cuda.current_stream()
-    pp.pack()
-    pp.attend()
+    log("[bench] long prefill: settle and warmup")
+    settle(torch, lambda: (pp.pack(), pp.attend()))
     for _ in range(warmup):
         pp.pack()
         pp.attend()
     evs = [Events(torch, 3) for _ in range(steps)]
     torch.cuda.synchronize()
+    log(f"[bench] long prefill: {steps} timed steps")
+    t0 = time.perf_counter()
     for e in evs:
         e.record(0, stream)
         pp.pack(stream)
@@ -219,16 +268,34 @@ def bench_prefill_long(torch, ops, synth, steps, warmup):
         pp.attend(stream)
         e.record(2, stream)
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     pack_ms = sum(e.ms(0, 1) for e in evs) / steps
     attn_ms = sum(e.ms(1, 2) for e in evs) / steps
     assert torch.isfinite(pp.o.float()).all().item(), "non-finite long prefill output"
     flops = B * Hq * causal_pairs(N, N) * 4.0 * d
-    tf = flops / (attn_ms * 1e-3) / 1e12
-    del pp, q, k, v
-    return dict(workload=w["name"], steps=steps, pack_kv_ms=round(pack_ms, 3), attention_ms=round(attn_ms, 3),
-                algorithmic_flops=flops,
-                value=round(flops / ((pack_ms + attn_ms) * 1e-3) / 1e12, 1), unit="TFLOP/s",
-                attention_tflops=round(tf, 1), frac_of_mixed_peak=round(tf / PEAK_MIXED_TFLOPS, 4))
+    del pp
+    # the other probability formats of the default bar on the same inputs
+    modes = {}
+    for name, pm in (("fp8_two_term", ops.P_FP8_TWO_TERM), ("bf16", ops.P_BF16)):
+        ppm = ops.PackedPrefill(q, k, v, causal=True, softmax_scale=1.0 / math.sqrt(d), v_tile_rows=w["v_tile_rows"],
+                                p_mode=pm)
+        ppm.pack()
+        ppm.attend()
+        n = max(2, steps // 4)
+        evm = [Events(torch, 3) for _ in range(n)]
+        torch.cuda.synchronize()
+        for e in evm:
+            e.record(0, stream)
+            ppm.pack(stream)
+            e.record(1, stream)
+            ppm.attend(stream)
+            e.record(2, stream)
+        torch.cuda.synchronize()
+        modes[name] = dict(steps=n, pack_ms=sum(e.ms(0, 1) for e in evm) / n, attn_ms=sum(e.ms(1, 2) for e in evm) / n)
+        assert torch.isfinite(ppm.o.float()).all().item(), f"non-finite long {name} output"
+        del ppm
+    del q, k, v
+    return dict(w=w, pack_ms=pack_ms, attn_ms=attn_ms, flops=flops, wall_ms=wall * 1e3 / steps, modes=modes)
 
 
 def build_cache(torch, ops, w, seed):
@@ -385,26 +452,147 @@ def bench_append_prefill(torch, ops, synth, steps, warmup):
     return out
 
 
-def cpu_baseline(synth):
-    """The oracle as it stands, timed on the whole prefill step (all 4 batches,
-    32 query / 8 KV heads, 4096 positions): about 15 s of host work."""
+def cpu_baseline(synth, kv_heads=(0, 5), rows_per_head=64):
+    """The oracle as it stands, timed on a bounded sample of the headline
+    workload (131072-token causal prefill, 64 query / 8 KV heads) and
+    extrapolated to the whole step.  The sample: two KV heads (their K/V
+    quantized in full, as the oracle's prefill does) and 64 seeded query rows
+    of each of their 16 query heads (1024 rows, rows 0 and N-1 and 128-key
+    tile edges included), each row attending to its full causal prefix.  The
+    oracle's cost is K/V quantization per KV head plus, per query row, a
+    product with all N keys (it masks after the product), so the full step is
+    extrapolated as 8/2 x the K/V part plus 64*N/1024 x the row part.  The row
+    part is timed again on one BLAS thread (one query head's rows)."""
     import numpy as np
     from oracle import attention as oatt
+    from oracle import quant
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     except Exception:
-        cores = 1
-    w = synth.WORKLOADS[2]
-    q, k, v = synth.prefill_inputs(2)
-    t0 = time.perf_counter()
-    o, _ = oatt.qk4v8_prefill(q, k, v, 1.0 / math.sqrt(w["d"]), True, w["v_tile_rows"])
-    dt = time.perf_counter() - t0
-    assert np.isfinite(o).all()
-    flops = w["B"] * w["Hq"] * causal_pairs(w["Nq"], w["Nk"]) * 4.0 * w["d"]
-    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"the whole causal GQA prefill step (B{w['B']} Hq{w['Hq']} Hkv{w['Hkv']} N{w['Nq']} "
-                       f"d{w['d']}): {dt:.1f} s of numpy fp64 including the quantizers")
+        threadpool_limits, cores = None, 1
+    w = synth.WORKLOADS[4]
+    N, d, Hq, Hkv, R = w["Nq"], w["d"], w["Hq"], w["Hkv"], w["v_tile_rows"]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    rng = np.random.default_rng([synth.ROOT_SEED, 4, 99])
+    t_kv = t_rows = t_rows_1 = 0.0
+    n_rows = rows_1 = 0
+    for h in kv_heads:
+        k = synth.prefill_k_slice(4, w, 0, h)
+        v = synth.normal_bits(4, synth.V_ID, 0, h, (N, d))
+        t0 = time.perf_counter()
+        kh = quant.dequantize_qk(*quant.quantize_qk(k))
+        vc, vs = quant.quantize_v(v[None], R)
+        vh = quant.dequantize_v(vc, vs, R)[0]
+        t_kv += time.perf_counter() - t0
+        for hq in range(h * G, (h + 1) * G):
+            rows = np.unique(np.concatenate([[0, 127, 128, N - 1], rng.integers(0, N, rows_per_head)]))[:rows_per_head]
+            qb = synth.normal_bits(4, synth.Q_ID, 0, hq, (N, d))[rows]
+            t0 = time.perf_counter()
+            qh = quant.dequantize_qk(*quant.quantize_qk(qb))
+            o, _ = oatt.attention(qh[None, None], kh[None, None], vh[None, None], scale, True, rows=(rows, N))
+            t_rows += time.perf_counter() - t0
+            n_rows += len(rows)
+            assert np.isfinite(o).all()
+            if threadpool_limits is not None and rows_1 == 0:
+                with threadpool_limits(limits=1):
+                    t0 = time.perf_counter()
+                    qh = quant.dequantize_qk(*quant.quantize_qk(qb))
+                    oatt.attention(qh[None, None], kh[None, None], vh[None, None], scale, True, rows=(rows, N))
+                    t_rows_1 += time.perf_counter() - t0
+                rows_1 = len(rows)
+    flops = w["B"] * Hq * causal_pairs(N, N) * 4.0 * d
+    full_s = t_kv * Hkv / len(kv_heads) + t_rows * (Hq * N) / n_rows
+    out = dict(value=round(flops / full_s / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
+               extrapolated=True, extrapolated_full_step_s=round(full_s, 1),
+               sample=f"the long causal prefill ({w['name']}): {n_rows} query rows of {len(kv_heads) * G} query "
+                      f"heads over their full causal prefix, and the K/V quantization of their {len(kv_heads)} KV "
+                      f"heads: {t_kv + t_rows:.1f} s of numpy fp64, extrapolated to the whole step "
+                      f"({full_s:.0f} s)")
+    if rows_1:
+        full_1 = t_kv * Hkv / len(kv_heads) + t_rows_1 * (Hq * N) / rows_1
+        out["one_thread"] = dict(value=round(flops / full_1 / 1e12, 6), unit="TFLOP/s", cores=1,
+                                 extrapolated_full_step_s=round(full_1, 1),
+                                 sample=f"{rows_1} query rows on one BLAS thread ({t_rows_1:.1f} s); the K/V part "
+                                        "as measured above")
+    return out
+
+
+def bench_quantizers(torch, ops, kd, vd, steps, warmup):
+    """The standalone quantizers on the causal GQA workload's K and V (batch 4,
+    8 KV heads, 4096 tokens, head_dim 128), in GB/s of algorithmic bytes:
+    quantize_qk reads 2d and writes d/2 + d/32 bytes per row; quantize_v reads
+    2d and writes d bytes per row plus one scale byte per V tile."""
+    B, H, N, d = kd.shape
+    rows = B * H * N
+    vg = vd.reshape(B * H, N, d)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, run, nbytes in (
+            ("quantize_qk", lambda: ops.quantize_qk(kd), rows * (2 * d + d // 2 + d // 32)),
+            ("quantize_v", lambda: ops.quantize_v(vg, 256), rows * (2 * d + d) + B * H * (-(-N // 256)))):
+        settle(torch, run, seconds=0.2)
+        for _ in range(warmup):
+            run()
+        evs = [Events(torch, 2) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in evs:
+            e.record(0, stream)
+            run()
+            e.record(1, stream)
+        torch.cuda.synchronize()
+        ms = sum(e.ms(0, 1) for e in evs) / steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = dict(us=round(ms * 1e3, 2), bytes=nbytes, value=round(gbs, 1), unit="GB/s",
+                         frac=round(gbs / PEAK_HBM_GBS, 4))
+    out["workload"] = f"causal_gqa_prefill K/V: B{B} Hkv{H} N{N} d{d} (V tiles of 256 rows)"
+    return out
+
+
+def bench_peaks(torch):
+    """Measured peaks of this GPU: a 4 GiB streaming read, the scaled FP4 and
+    FP8 32x32x64 MFMA issued back to back on every CU, and v_exp_f32."""
+    from bit_quantized_attention_online_amd import peaks
+    dev = torch.device("cuda:0")
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(1 << 20, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def best(run, reps=10):
+        for _ in range(3):
+            run()
+        times = []
+        for _ in range(reps):
+            e = Events(torch, 2)
+            e.record(0, stream)
+            work = run()
+            e.record(1, stream)
+            torch.cuda.synchronize()
+            times.append(e.ms(0, 1))
+        return work, min(times), sorted(times)[len(times) // 2]
+
+    settle(torch, lambda: peaks.hbm_read(buf, sink), seconds=0.3)
+    nb, t_best, t_med = best(lambda: peaks.hbm_read(buf, sink))
+    out = dict(hbm_read=dict(bytes=nb, best_GBs=round(nb / (t_best * 1e-3) / 1e9, 1),
+                             median_GBs=round(nb / (t_med * 1e-3) / 1e9, 1), nominal_GBs=PEAK_HBM_GBS))
+    del buf
+    for name, fmt, nominal in (("mfma_fp4", peaks.FMT_FP4, PEAK_FP4_TFLOPS),
+                               ("mfma_fp8", peaks.FMT_FP8, PEAK_FP8_TFLOPS),
+                               ("mfma_bf16", peaks.FMT_BF16, PEAK_BF16_TFLOPS)):
+        fl, t_best, t_med = best(lambda: peaks.mfma(fmt, 20000, sink))
+        out[name] = dict(flops=fl, best_TFLOPs=round(fl / (t_best * 1e-3) / 1e12, 1),
+                         median_TFLOPs=round(fl / (t_med * 1e-3) / 1e12, 1), nominal_TFLOPs=nominal)
+    ex, t_best, t_med = best(lambda: peaks.exp2(20000, sink))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    clock_ghz = 2.4
+    out["exp2"] = dict(exps=ex, best_Gexp_per_s=round(ex / (t_best * 1e-3) / 1e9, 1),
+                       lanes_per_cu_cycle_at_2p4GHz=round(ex / (t_best * 1e-3) / (cus * clock_ghz * 1e9), 2))
+    p4, p8, pb = out["mfma_fp4"]["best_TFLOPs"], out["mfma_fp8"]["best_TFLOPs"], out["mfma_bf16"]["best_TFLOPs"]
+    out["mixed_fp4_fp8_TFLOPs"] = round(2.0 / (1.0 / p4 + 1.0 / p8), 1)
+    out["mixed_fp4_bf16_TFLOPs"] = round(2.0 / (1.0 / p4 + 1.0 / pb), 1)
+    return out
 
 
 def calib_copy(torch, nbytes=1 << 30):
@@ -416,13 +604,36 @@ def calib_copy(torch, nbytes=1 << 30):
     torch.cuda.synchronize()
 
 
+PARTS = ("long", "gqa", "decode", "verify", "append", "quant", "peaks")
+
+
+def mode_objects(res):
+    """Step and attention throughput of each probability format timed on a
+    prefill workload (same inputs, same algorithmic flops), against the
+    format's own mixed roofline and against the FP4/FP8 one."""
+    from bit_quantized_attention_online_amd import ops
+    out = {}
+    for name, m in res["modes"].items():
+        pm = ops.P_BF16 if name == "bf16" else ops.P_FP8_TWO_TERM
+        tf = res["flops"] / (m["attn_ms"] * 1e-3) / 1e12
+        out[name] = {"p_mode": pm, "dtype": MODE_DTYPE[pm], "pack_kv_ms": round(m["pack_ms"], 4),
+                     "attention_ms": round(m["attn_ms"], 4),
+                     "value": round(res["flops"] / ((m["pack_ms"] + m["attn_ms"]) * 1e-3) / 1e12, 1),
+                     "attention_tflops": round(tf, 1), "unit": "TFLOP/s", "peak": round(mode_peak(pm), 1),
+                     "frac": round(tf / mode_peak(pm), 4),
+                     "frac_of_fp4_fp8_mixed_peak": round(tf / PEAK_MIXED_TFLOPS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20, help="timed steps of the headline (131072-token) prefill")
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--peaks", action="store_true", help="also measure HBM / MFMA / exp2 peaks of this GPU")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated subset of " + ",".join(PARTS) + " (for short profiled runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -430,68 +641,112 @@ def main():
         print("bench.py measures one GPU only: the QK4V8 path here has no multi-GPU mode "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    parts = set(PARTS) if args.only is None else set(args.only.split(","))
+    bad = parts - set(PARTS)
+    if bad:
+        print(f"unknown --only parts {sorted(bad)}; choose from {PARTS}", file=sys.stderr)
+        sys.exit(2)
     import torch
     from bit_quantized_attention_online_amd import ops, synth
     ops.lib()
     if args.calib_copy:
         calib_copy(torch)
-
-    pf = bench_prefill(torch, ops, synth, args.steps, args.warmup)
-    step_ms = pf["pack_ms"] + pf["attn_ms"]
-    value = pf["flops"] / (step_ms * 1e-3) / 1e12
-    attn_tflops = pf["flops"] / (pf["attn_ms"] * 1e-3) / 1e12
-    traffic = measured_traffic(TRAFFIC_FILE, ATTN_SOURCE)
+    short_steps = max(args.steps, 50)      # sub-millisecond kernels: more steps per measurement
+    short_warmup = max(args.warmup, 10)
     line = {
         "metric": "QK4V8 attn: prefill TFLOP/s + decode KV GB/s, % of MI355X roofline",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "mxfp4xmxfp4+fp8xfp8->fp32",
-        "data": "synthetic",
-        "config": {"workload": pf["w"]["name"], "batch": pf["w"]["B"], "q_heads": pf["w"]["Hq"],
-                   "kv_heads": pf["w"]["Hkv"], "seq_len": pf["w"]["Nq"], "head_dim": pf["w"]["d"],
-                   "causal": True, "v_tile_rows": pf["w"]["v_tile_rows"],
-                   "algorithmic_flops": pf["flops"]},
-        "wall_ms_per_step": round(pf["wall_ms"], 4),
-        "prefill_breakdown_ms": {"pack_kv": round(pf["pack_ms"], 4), "attention": round(pf["attn_ms"], 4)},
-        "prefill_fast_mode": {"p_terms": 1, "attention_ms": round(pf["fast_ms"], 4),
-                              "value": round(pf["flops"] / (pf["fast_ms"] * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
-                              "frac_of_mixed_peak": round(pf["flops"] / (pf["fast_ms"] * 1e-3) / 1e12
-                                                          / PEAK_MIXED_TFLOPS, 4),
-                              "note": "single-term E4M3 probabilities; about 2e-2 relative L2 from exact attention, "
-                                      "outside the 5e-3 gate of the default path"},
-        "prefill_sliding_window": {"window": SWA_WINDOW, "attention_ms": round(pf["swa"]["ms"], 4),
-                                   "algorithmic_flops": pf["swa"]["flops"],
-                                   "value": round(pf["swa"]["flops"] / (pf["swa"]["ms"] * 1e-3) / 1e12, 1),
-                                   "unit": "TFLOP/s",
-                                   "frac_of_mixed_peak": round(pf["swa"]["flops"] / (pf["swa"]["ms"] * 1e-3) / 1e12
-                                                               / PEAK_MIXED_TFLOPS, 4)},
-        "prefill_hadamard": {"hadamard": 1, "pack_kv_ms": round(pf["had"]["pack_ms"], 4),
-                             "attention_ms": round(pf["had"]["attn_ms"], 4),
-                             "value": round(pf["flops"] / ((pf["had"]["pack_ms"] + pf["had"]["attn_ms"]) * 1e-3)
-                                            / 1e12, 1), "unit": "TFLOP/s"},
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel<128,causal>",
-                     "achieved": round(attn_tflops, 1), "peak": round(PEAK_MIXED_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_MIXED_TFLOPS, 4), "traffic": traffic},
+        "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": MODE_DTYPE[ops.P_DEFAULT_MODE], "data": "synthetic",
     }
-    if not args.skip_decode:
-        line["decode"] = bench_decode(torch, ops, synth, 3, args.steps, args.warmup)
+    default_peak = mode_peak(ops.P_DEFAULT)
+    if "long" in parts:
+        pl = bench_prefill_long(torch, ops, synth, args.steps, args.warmup)
+        w = pl["w"]
+        step_ms = pl["pack_ms"] + pl["attn_ms"]
+        attn_tf = pl["flops"] / (pl["attn_ms"] * 1e-3) / 1e12
+        line.update({
+            "value": round(pl["flops"] / (step_ms * 1e-3) / 1e12, 2),
+            "ms_per_step": round(step_ms, 3),
+            "config": {"workload": w["name"], "batch": w["B"], "q_heads": w["Hq"], "kv_heads": w["Hkv"],
+                       "seq_len": w["Nq"], "head_dim": w["d"], "causal": True, "v_tile_rows": w["v_tile_rows"],
+                       "k_outlier_rows": w["k_outlier_row_frac"], "algorithmic_flops": pl["flops"]},
+            "wall_ms_per_step": round(pl["wall_ms"], 3),
+            "prefill_breakdown_ms": {"pack_kv": round(pl["pack_ms"], 4), "attention": round(pl["attn_ms"], 3)},
+            "roofline": {"bound": "mfma", "kernel": f"attn_kernel<128,causal,p_mode={ops.P_DEFAULT_MODE}>",
+                         "achieved": round(attn_tf, 1), "peak": round(default_peak, 1), "unit": "TFLOP/s",
+                         "frac": round(attn_tf / default_peak, 4),
+                         "frac_of_fp4_fp8_mixed_peak": round(attn_tf / PEAK_MIXED_TFLOPS, 4),
+                         "traffic": measured_traffic(LONG_TRAFFIC_FILE, ATTN_SOURCE)},
+            "p_modes": mode_objects(pl),
+        })
         torch.cuda.empty_cache()
-        line["block_verify"] = bench_decode(torch, ops, synth, 5, args.steps, args.warmup)
+    keep = {}
+    if "gqa" in parts:
+        pf = bench_prefill(torch, ops, synth, short_steps, short_warmup, keep=keep)
+        wq = pf["w"]
+        step_ms = pf["pack_ms"] + pf["attn_ms"]
+        attn_tf = pf["flops"] / (pf["attn_ms"] * 1e-3) / 1e12
+        fast_tf = pf["flops"] / (pf["fast_ms"] * 1e-3) / 1e12
+        line["prefill_causal_gqa"] = {
+            "workload": wq["name"], "steps": short_steps, "value": round(pf["flops"] / (step_ms * 1e-3) / 1e12, 1),
+            "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4), "algorithmic_flops": pf["flops"],
+            "breakdown_ms": {"pack_kv": round(pf["pack_ms"], 4), "attention": round(pf["attn_ms"], 4)},
+            "roofline": {"bound": "mfma", "kernel": f"attn_kernel<128,causal,p_mode={ops.P_DEFAULT_MODE}>",
+                         "achieved": round(attn_tf, 1), "peak": round(default_peak, 1), "unit": "TFLOP/s",
+                         "frac": round(attn_tf / default_peak, 4),
+                         "frac_of_fp4_fp8_mixed_peak": round(attn_tf / PEAK_MIXED_TFLOPS, 4),
+                         "traffic": measured_traffic(TRAFFIC_FILE, ATTN_SOURCE)},
+            "p_modes": mode_objects(pf),
+            "fast_mode": {"p_mode": 1, "attention_ms": round(pf["fast_ms"], 4), "value": round(fast_tf, 1),
+                          "unit": "TFLOP/s", "peak": round(PEAK_MIXED_TFLOPS, 1),
+                          "frac_of_mixed_peak": round(fast_tf / PEAK_MIXED_TFLOPS, 4),
+                          "note": "single-term E4M3 probabilities with a range exponent per 32-key block; about "
+                                  "2e-2 relative L2 from exact attention, outside the 5e-3 gate of the default "
+                                  "path"},
+            "hadamard": {"hadamard": 1, "pack_kv_ms": round(pf["had"]["pack_ms"], 4),
+                         "attention_ms": round(pf["had"]["attn_ms"], 4),
+                         "value": round(pf["flops"] / ((pf["had"]["pack_ms"] + pf["had"]["attn_ms"]) * 1e-3)
+                                        / 1e12, 1), "unit": "TFLOP/s"},
+            "sliding_window": {"window": SWA_WINDOW, "attention_ms": round(pf["swa"]["ms"], 4),
+                               "algorithmic_flops": pf["swa"]["flops"],
+                               "value": round(pf["swa"]["flops"] / (pf["swa"]["ms"] * 1e-3) / 1e12, 1),
+                               "unit": "TFLOP/s",
+                               "frac": round(pf["swa"]["flops"] / (pf["swa"]["ms"] * 1e-3) / 1e12 / default_peak, 4)},
+        }
+    if "quant" in parts:
+        if "k" not in keep:
+            q, k, v = synth.prefill_inputs(2)
+            to = lambda a: torch.from_numpy(a.view("int16")).cuda().view(torch.bfloat16)
+            keep.update(k=to(k), v=to(v))
+            del q
+        line["quantizers"] = bench_quantizers(torch, ops, keep["k"], keep["v"], short_steps, short_warmup)
+    keep.clear()
+    torch.cuda.empty_cache()
+    if "decode" in parts:
+        line["decode"] = bench_decode(torch, ops, synth, 3, short_steps, short_warmup)
         torch.cuda.empty_cache()
-        line["kv_append_prompt"] = bench_append_prefill(torch, ops, synth, args.steps, args.warmup)
+    if "verify" in parts:
+        line["block_verify"] = bench_decode(torch, ops, synth, 5, short_steps, short_warmup)
         torch.cuda.empty_cache()
-        # ~0.25 s per step: a few steps are enough
-        line["prefill_long"] = bench_prefill_long(torch, ops, synth, min(args.steps, 5), min(args.warmup, 2))
+    if "append" in parts:
+        line["kv_append_prompt"] = bench_append_prefill(torch, ops, synth, short_steps, short_warmup)
         torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host")
+    if args.peaks and "peaks" in parts:
+        log("[bench] measuring the GPU's peaks")
+        pk = bench_peaks(torch)
+        line["measured_peaks"] = pk
+        measured_mixed = pk["mixed_fp4_bf16_TFLOPs"] if ops.P_DEFAULT_MODE == ops.P_BF16 else \
+            pk["mixed_fp4_fp8_TFLOPs"]
+        for obj in (line.get("roofline"), line.get("prefill_causal_gqa", {}).get("roofline")):
+            if obj:
+                obj["frac_of_measured_peak"] = round(obj["achieved"] / measured_mixed, 4)
+        for key in ("decode", "block_verify"):
+            if key in line:
+                line[key]["roofline"]["frac_of_measured_peak"] = round(line[key]["roofline"]["achieved"]
+                                                                       / pk["hbm_read"]["best_GBs"], 4)
+    if not args.no_cpu_baseline and "long" in parts:
+        log("[bench] timing the oracle on the host (a bounded sample of the long prefill)")
         line["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(line), flush=True)
 

@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqk4v8.so")
 SOURCES = ["qk4v8_api.hip", "quantize.hip", "prefill.hip", "decode.hip", "append.hip"]
+# the peak microbenchmarks (include/qk4v8_peaks.h) are a library of their own
+PEAKS_LIB = os.path.join(PKG, "libqk4v8_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 
 
@@ -46,20 +49,26 @@ def _compile(src):
     return obj, msgs
 
 
-def build(verbose=False):
-    """Compile every HIP source for gfx950 and link libqk4v8.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for _, msgs in results:
-        if verbose and msgs.strip():
-            print(msgs, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile every HIP source for gfx950 and link libqk4v8.so and
+    libqk4v8_peaks.so (always rebuilds)."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        results = list(ex.map(_compile, SOURCES + PEAKS_SOURCES))
+    for _, msgs in results:
+        if verbose and msgs.strip():
+            print(msgs, file=sys.stderr)
+    _link([o for o, _ in results[:len(SOURCES)]], LIB)
+    _link([o for o, _ in results[len(SOURCES):]], PEAKS_LIB)
     return LIB
 
 

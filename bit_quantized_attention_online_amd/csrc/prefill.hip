@@ -106,25 +106,30 @@ __device__ __forceinline__ void keep_in_vgprs(const T& x) {
 
 }  // namespace
 
-// Bytes of one packed 128-key tile record (the LDS image of the tile).
-template <int D>
+// Bytes of one packed 128-key tile record (the LDS image of the tile).  BV:
+// V^T as bf16 values (the E4M3 codes times the tile's E8M0 scale, exact)
+// for the bf16 P·V product, else as E4M3 codes.
+template <int D, bool BV = false>
 struct TileBytes {
   static constexpr int NS = D / 64;               // 64-wide contraction steps of QK^T
   static constexpr int K = 4 * NS * 1024;         // K codes: [kb][step][lane][16 B]
   static constexpr int SC = 1024;                 // K scales [lane][kb*NS+step], then the V scale word
   static constexpr int KS = 64 * 4 * NS;          // K scale bytes at the start of SC
   static constexpr int VS_OFF = 512;              // V scale word inside SC
-  static constexpr int V = kKvTile * D;           // V^T codes
+  static constexpr int V = kKvTile * D * (BV ? 2 : 1);   // V^T codes (or bf16 values)
   static constexpr int REC = K + SC + V;          // a multiple of 1 KB
   static constexpr int CHUNKS = REC / 1024;       // 1 KB direct-load chunks
 };
 
-PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, int v_tile_rows) {
+PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, int v_tile_rows, bool bf16_v) {
   PrefillLayout L;
   const int64_t bk = (int64_t)batch * kv_heads;
   L.n_tiles = (seq_k + kKvTile - 1) / kKvTile;
   L.n_vtiles = (seq_k + v_tile_rows - 1) / v_tile_rows;
-  L.rec_bytes = head_dim == 64 ? TileBytes<64>::REC : TileBytes<128>::REC;
+  if (head_dim == 64)
+    L.rec_bytes = bf16_v ? TileBytes<64, true>::REC : TileBytes<64>::REC;
+  else
+    L.rec_bytes = bf16_v ? TileBytes<128, true>::REC : TileBytes<128>::REC;
   size_t off = 0;
   L.off_rec = off;   off = align_up(off + (size_t)bk * L.n_tiles * L.rec_bytes);
   L.off_vtile = off; off = align_up(off + (size_t)bk * L.n_vtiles);
@@ -140,11 +145,11 @@ PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, i
 //   codes : [kb][s][lane = rho + 32h][16 B]          at 0
 //   scales: [lane][kb*NS + s]                         at K
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool BV>
 __device__ __forceinline__ void pack_k_block(const uint16_t* __restrict__ k, int64_t ks0, int64_t ks1, int64_t ks2,
                                              int kv_heads, int seq_k, int64_t n_tiles, uint8_t* __restrict__ rec,
                                              int hadamard, int64_t id) {
-  using TB = TileBytes<D>;
+  using TB = TileBytes<D, BV>;
   constexpr int NB = D / 32, NS = D / 64;
   const int g = (int)(id % NB);
   const int64_t jj = (id / NB) % (n_tiles * kKvTile);
@@ -190,12 +195,12 @@ __device__ __forceinline__ void pack_k_block(const uint16_t* __restrict__ k, int
   r[TB::K + lane * (4 * NS) + kb * NS + step] = (uint8_t)scale;
 }
 
-template <int D>
+template <int D, bool BV>
 __global__ void __launch_bounds__(256) pack_k_kernel(const uint16_t* __restrict__ k, int64_t ks0, int64_t ks1,
                                                      int64_t ks2, int kv_heads, int seq_k, int64_t n_tiles,
                                                      uint8_t* __restrict__ rec, int64_t total, int hadamard) {
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id < total) pack_k_block<D>(k, ks0, ks1, ks2, kv_heads, seq_k, n_tiles, rec, hadamard, id);
+  if (id < total) pack_k_block<D, BV>(k, ks0, ks1, ks2, kv_heads, seq_k, n_tiles, rec, hadamard, id);
 }
 
 // ---------------------------------------------------------------------------
@@ -248,12 +253,12 @@ struct PackVShared {
   uint8_t own[4];                        // E8M0 of this tile's V tiles (FUSED)
 };
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool BV>
 __device__ __forceinline__ void pack_v_tile(const uint16_t* __restrict__ v, int64_t vs0, int64_t vs1, int64_t vs2,
                                             int kv_heads, int seq_k, int R, int64_t n_tiles, int64_t n_vtiles,
                                             const uint8_t* __restrict__ vtile, uint8_t* __restrict__ rec,
                                             int64_t blk, PackVShared<D>& sh) {
-  using TB = TileBytes<D>;
+  using TB = TileBytes<D, BV>;
   constexpr int LDSROW = PackVShared<D>::LDSROW;
   constexpr int CPR = D / 8;
   constexpr int PER = kKvTile * CPR / 256;   // 16-byte chunks per thread (rows tid/CPR + (256/CPR)*i)
@@ -321,6 +326,39 @@ __device__ __forceinline__ void pack_v_tile(const uint16_t* __restrict__ v, int6
   __syncthreads();
   uint8_t* const r = rec + (bk * n_tiles + tile) * TB::REC;
   uint8_t* out = r + TB::K + TB::SC;
+  if constexpr (BV) {
+    // bf16 V^T in the operand order of the 32x32x16 bf16 MFMA: chunk
+    // [db][st][lane = m + 32h] holds column 32*db + m at the 8 keys
+    // 32*(st/2) + 16*h + 8*(st%2) .. +7, each the E4M3 value times 2^X_V of
+    // its V tile, exact in fp32 and then in bf16 (bf16 keeps fp32's exponent
+    // range; only values below 2^-126 round, by at most 2^-134).  Keys past
+    // seq_k have zero codes.
+    for (int o = threadIdx.x; o < D * 16; o += 256) {
+      const int lane = o & 63, st = (o >> 6) & 7, db = o >> 9;
+      const int col = db * 32 + (lane & 31), k0 = 32 * (st >> 1) + 16 * (lane >> 5) + 8 * (st & 1);
+      int64_t j = tile * kKvTile + k0;
+      if (j >= seq_k) j = seq_k - 1;
+      const int X = (int)(FUSED ? own[k0 / R] : vts[j / R]) - 127;
+      const float s1 = exp2i(X / 2), s2 = exp2i(X - X / 2);   // each factor in range for X = -127
+      uint32_t wv[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc |= (uint32_t)tileb[(k0 + 4 * q + e) * LDSROW + col] << (8 * e);
+        wv[q] = acc;
+      }
+      uint32_t outw[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[q], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[q], true);
+        outw[2 * q] = bf16x2(lo[0] * s1 * s2, lo[1] * s1 * s2);
+        outw[2 * q + 1] = bf16x2(hi[0] * s1 * s2, hi[1] * s1 * s2);
+      }
+      *reinterpret_cast<uint4*>(out + (int64_t)o * 16) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    }
+  } else
   for (int o = threadIdx.x; o < D * 8; o += 256) {
     const int lane = o & 63, half = (o >> 6) & 1, s2 = (o >> 7) & 1, db = o >> 8;
     const int col = db * 32 + (lane & 31), k0 = 64 * s2 + 32 * half + 16 * (lane >> 5);
@@ -346,13 +384,13 @@ __device__ __forceinline__ void pack_v_tile(const uint16_t* __restrict__ v, int6
   }
 }
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool BV>
 __global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict__ v, int64_t vs0, int64_t vs1,
                                                      int64_t vs2, int kv_heads, int seq_k, int R, int64_t n_tiles,
                                                      int64_t n_vtiles, const uint8_t* __restrict__ vtile,
                                                      uint8_t* __restrict__ rec) {
   __shared__ PackVShared<D> sh;
-  pack_v_tile<D, FUSED>(v, vs0, vs1, vs2, kv_heads, seq_k, R, n_tiles, n_vtiles, vtile, rec, blockIdx.x, sh);
+  pack_v_tile<D, FUSED, BV>(v, vs0, vs1, vs2, kv_heads, seq_k, R, n_tiles, n_vtiles, vtile, rec, blockIdx.x, sh);
 }
 
 // Both packs in one launch (V tiles of R <= 128 rows, whose scales the V
@@ -369,16 +407,17 @@ struct PackKVArgs {
   uint8_t* rec;
 };
 
-template <int D>
+template <int D, bool BV>
 __global__ void __launch_bounds__(256) pack_kv_kernel(PackKVArgs a) {
   __shared__ PackVShared<D> sh;
   if ((int64_t)blockIdx.x < a.nblk_k) {
     const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (id < a.total_k) pack_k_block<D>(a.k, a.ks0, a.ks1, a.ks2, a.kv_heads, a.seq_k, a.n_tiles, a.rec, a.hadamard, id);
+    if (id < a.total_k)
+      pack_k_block<D, BV>(a.k, a.ks0, a.ks1, a.ks2, a.kv_heads, a.seq_k, a.n_tiles, a.rec, a.hadamard, id);
     return;
   }
-  pack_v_tile<D, true>(a.v, a.vs0, a.vs1, a.vs2, a.kv_heads, a.seq_k, a.R, a.n_tiles, a.n_vtiles, a.vtile, a.rec,
-                       (int64_t)blockIdx.x - a.nblk_k, sh);
+  pack_v_tile<D, true, BV>(a.v, a.vs0, a.vs1, a.vs2, a.kv_heads, a.seq_k, a.R, a.n_tiles, a.n_vtiles, a.vtile, a.rec,
+                           (int64_t)blockIdx.x - a.nblk_k, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -430,15 +469,33 @@ struct AttnArgs {
 // its chunks of tile T+1 have landed (the loads complete in order, so at most
 // its chunks of tile T+2 may still be in flight), which publishes tile T+1
 // before its first QK^T.  A tile thus has about three phases to arrive.
-// FAST: single-term E4M3 probabilities (integral running maximum, no lo term).
-template <int D, bool CAUSAL, bool FAST>
+// (Measured: group 1's MFMA phase, which ends with its wait, runs some 400
+// cycles longer than group 0's; running the feed three tiles ahead in five
+// stages left that gap unchanged, so it is not the loads' latency.)
+// PM = kPSingle: single-term E4M3 probabilities (integral running maximum, no
+// lo term).  PM = kPBf16: bf16 probabilities on the bf16 matrix core against
+// V^T stored as exact bf16 values; its records are 16 KB larger at head_dim
+// 128, so three LDS stages hold them (41 KB each) and the feed runs one tile
+// ahead: the four waves of group 0 copy all of stream tile T+1 at the start of
+// their MFMA phase for tile T, into the stage of tile T-2, whose last reader
+// (group 1's P·V) ran in the phase before, and wait for it at the barrier
+// that ends their VALU phase, so a tile has two phases to arrive.  Group 1
+// copies nothing.  Measured: a direct load costs the issuing wave some 20 - 45
+// cycles in an MFMA phase but about 90 inside a VALU phase, which in this
+// mode is the longer one, where group 1 would have to issue; splitting each
+// tile between both groups' MFMA phases instead (the V part is needed one
+// iteration after the K part) left group 1 waiting some 1700 cycles per
+// phase for its copies, with the records in L2 or not.
+template <int D, bool CAUSAL, int PM>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_kernel(AttnArgs a) {
-  using TB = TileBytes<D>;
+  constexpr bool FAST = PM == kPSingle;
+  constexpr bool BF = PM == kPBf16;
+  using TB = TileBytes<D, BF>;
   constexpr int NS = TB::NS;        // QK^T contraction steps (64 head_dim each)
   constexpr int NDB = D / 32;       // 32-row head_dim blocks of O^T
-  constexpr int kStages = 4;
-  constexpr int kOnes = kStages * TB::REC;   // 1 KB of E4M3 1.0: the row-sum MFMA operand
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * TB::REC + 1024];
+  constexpr int kStages = BF ? 3 : 4;
+  constexpr int kOnes = kStages * TB::REC;   // 1 KB of E4M3 1.0: the row-sum MFMA operand (FP8 modes)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * TB::REC + (BF ? 0 : 1024)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -513,11 +570,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto stage_of = [&](int k) -> uint32_t { return (g0 + (uint32_t)k) % kStages; };
 
   // ---- tile feed: direct global->LDS loads of 1 KB chunks, two tiles ahead
-  // of the QK^T along the stream of this workgroup's items; wave w copies
-  // chunks w, w+8, ... of each tile record ----
-  const int my_chunks = (TB::CHUNKS - wave + kWaves - 1) / kWaves;
+  // of the QK^T (one in bf16 mode) along the stream of this workgroup's
+  // items; wave w copies chunks w, w+8, ... of each tile record ----
+  // chunks this wave copies per tile: every 8th of the record, or in bf16
+  // mode every 4th for the waves of group 0 and none for group 1
+  constexpr int kFeeders = BF ? kWaves / 2 : kWaves;
+  const int my_chunks = BF && wave >= kFeeders ? 0 : (TB::CHUNKS - wave + kFeeders - 1) / kFeeders;
   // feed state: the next record to copy, the copies left in its item, the
-  // LDS stage it goes to (its stream index mod 4)
+  // LDS stage it goes to (its stream index mod kStages)
   int feed_i = 0;
   const uint8_t* feed_src = nullptr;
   int feed_left = 0;
@@ -535,14 +595,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto feed = [&]() -> bool __attribute__((always_inline)) {
     if (feed_left == 0) return false;   // past the last item
     uint8_t* dst = lds + feed_stage * TB::REC;
-    static_for<(TB::CHUNKS + kWaves - 1) / kWaves>([&](auto I) {
+    static_for<(TB::CHUNKS + kFeeders - 1) / kFeeders>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      const int c = wave + kWaves * i;
-      if (kWaves * (i + 1) <= TB::CHUNKS || c < TB::CHUNKS)
+      const int c = wave + kFeeders * i;
+      if (kFeeders * (i + 1) <= TB::CHUNKS || c < TB::CHUNKS)
         buffer_to_lds16(feed_src, TB::REC, (uint32_t)(c * 1024 + lane * 16), dst + c * 1024);
     });
     feed_src += TB::REC;
-    feed_stage = (feed_stage + 1) & (kStages - 1);
+    feed_stage = feed_stage + 1 == kStages ? 0 : feed_stage + 1;
     if (--feed_left == 0) {
       ++feed_i;
       feed_item();
@@ -649,7 +709,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     L = v16f{};
     m_run = -INFINITY;
   };
-  v8i Phi[2] = {v8i{}, v8i{}}, Plo[2] = {v8i{}, v8i{}};
+  v8i Phi[2] = {v8i{}, v8i{}}, Plo[2] = {v8i{}, v8i{}};   // FP8 modes
+  v4i Pb[8];                                                 // bf16 mode: P^T operands of the 8 steps
   // E8M0 range exponent of the probabilities this lane supplies for P·V
   // steps 0 and 1 (the MFMA applies lane half h's byte to k-block h, the
   // keys 64*s2 + 32*h .. +31)
@@ -717,7 +778,40 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int i = 0; i < NS; ++i) ks[i] = ksw[i];
     };
-    if constexpr (PV) {
+    if constexpr (PV && BF) {
+      // bf16 P·V: head_dim block db, steps 4*half .. 4*half + 3 (16 keys
+      // each) form one unit of four MFMAs; the unit's V^T operands (16 B per
+      // lane and step, [db][st][lane] in the record) are read one unit ahead
+      const uint8_t* lv = lds + stage_of(k - 1) * TB::REC + TB::K + TB::SC + lane * 16;
+      v4i bv[2][4];
+      auto bvload = [&](auto U) __attribute__((always_inline)) {
+        constexpr int u = decltype(U)::value;
+        static_for<4>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          bv[u & 1][j] = *reinterpret_cast<const v4i*>(lv + ((u >> 1) * 8 + 4 * (u & 1) + j) * 1024);
+        });
+      };
+      constexpr uint32_t kBf16Ones = 0x3F803F80u;   // two bf16 1.0
+      const v4i ones = v4i{(int)kBf16Ones, (int)kBf16Ones, (int)kBf16Ones, (int)kBf16Ones};
+      bvload(std::integral_constant<int, 0>{});
+      static_for<2 * NDB + 1>([&](auto J) {
+        constexpr int u = decltype(J)::value;
+        if constexpr (u < 2 * NDB - 1) bvload(std::integral_constant<int, u + 1>{});
+        if constexpr (u == 2 * NDB && QK) kload();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (u < 2 * NDB) {
+          constexpr int db = u >> 1, h4 = 4 * (u & 1);
+          static_for<4>([&](auto JJ) {
+            constexpr int j = decltype(JJ)::value;
+            O[db] = mfma32x32x16_bf16(bv[u & 1][j], Pb[h4 + j], O[db]);
+          });
+        } else {
+          // row sums of the bf16 weights: 1·P^T
+          static_for<8>([&](auto ST) { L = mfma32x32x16_bf16(ones, Pb[decltype(ST)::value], L); });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else if constexpr (PV) {
       const uint8_t* base = lds + stage_of(k - 1) * TB::REC;
       const uint8_t* lv = base + TB::K + TB::SC + lane * 16;
       const uint32_t vsw = *reinterpret_cast<const uint32_t*>(base + TB::K + TB::VS_OFF);
@@ -780,7 +874,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[kb][i] = mask_range(S[kb][i], 32 * kb + i, low, row_span);
     }
-    if constexpr (FAST)
+    if constexpr (BF)
+      softmax_tile32_bf16<NDB>(S, cexp, m_run, O, L, Pb);
+    else if constexpr (FAST)
       softmax_tile32_single<NDB>(S, cexp, m_run, O, L, Phi, psc, lh);
     else
       softmax_tile32<NDB>(S, cexp, m_run, O, L, Phi, Plo, psc);
@@ -789,7 +885,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // one iteration of the schedule for tile k of the current item; the first
   // (no P·V yet) is peeled so the steady state has no branches
   auto iteration = [&](int k, auto with_pv) __attribute__((always_inline)) {
-    const int pending = feed() ? my_chunks : 0;
+    // stream tile T+2 (bf16 mode: T+1, copied by group 0 alone)
+    int pending = 0;
+    if constexpr (BF) {
+      if (grp == 0) feed();
+    } else {
+      pending = feed() ? my_chunks : 0;
+    }
     mfma_step(k, with_pv, std::true_type{});
     // The matrix instructions are pure values to the compiler, which would
     // otherwise sink them past the barrier into the other phase: an empty asm
@@ -802,15 +904,19 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     static_for<4>([&](auto KB) { keep_in_vgprs(S[decltype(KB)::value]); });
     // the next tile of the stream must have landed (from this wave) before the
     // barrier that ends the second phase of this iteration: group 1's MFMA
-    // phase, group 0's VALU phase
-    if (grp == 1) wait_dma(pending);
+    // phase, group 0's VALU phase (bf16 mode: group 0's copies of T+1)
+    if (!BF && grp == 1) wait_dma(pending);
     phase_barrier();
     valu_step(k);
-    static_for<2>([&](auto I) {
-      keep_in_vgprs(Phi[decltype(I)::value]);
-      if constexpr (!FAST) keep_in_vgprs(Plo[decltype(I)::value]);
-    });
-    if (grp == 0) wait_dma(pending);
+    if constexpr (BF) {
+      static_for<8>([&](auto I) { keep_in_vgprs(Pb[decltype(I)::value]); });
+    } else {
+      static_for<2>([&](auto I) {
+        keep_in_vgprs(Phi[decltype(I)::value]);
+        if constexpr (!FAST) keep_in_vgprs(Plo[decltype(I)::value]);
+      });
+    }
+    if (grp == 0) wait_dma(BF ? 0 : pending);
     phase_barrier();
   };
   // the item's last iteration (P·V of tile nt - 1 only): its MFMA phase also
@@ -833,19 +939,22 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     phase_barrier();
   };
 
-  // ---- first item: its rows, the stream's first two tiles ----
+  // ---- first item: its rows, the stream's first tiles ----
   int cur_i = 0;
   const int cur = seq_item(cur_i);
   setup(cur);
-  feed();
-  const int pending0 = feed() ? my_chunks : 0;
+  if (!BF || grp == 0) feed();
+  int pending0 = 0;
+  if constexpr (!BF) pending0 = feed() ? my_chunks : 0;   // tile 1 stays in flight
   {
     uint32_t wq[NS][16];
     load_q(cur, wq);
     quantize_q(wq);
   }
   reset_acc();
-  if (tid < 256) reinterpret_cast<uint32_t*>(lds + kOnes)[tid] = kFp8Ones;
+  if constexpr (!BF) {
+    if (tid < 256) reinterpret_cast<uint32_t*>(lds + kOnes)[tid] = kFp8Ones;
+  }
   wait_dma(pending0);                  // tile 0 (this wave's chunks)
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the ones operand is written
   phase_barrier();
@@ -867,9 +976,9 @@ static int gcd_int(int x, int y) {
   return x;
 }
 
-template <int D>
+template <int D, bool BV>
 static hipError_t launch_pack_d(const PrefillParams& p, hipStream_t stream) {
-  const PrefillLayout L = prefill_layout(p.batch, p.kv_heads, p.seq_k, D, p.v_tile_rows);
+  const PrefillLayout L = prefill_layout(p.batch, p.kv_heads, p.seq_k, D, p.v_tile_rows, BV);
   uint8_t* wvt = p.ws + L.off_vtile;
   const int64_t bk = (int64_t)p.batch * p.kv_heads;
   const int64_t total_k = bk * L.n_tiles * kKvTile * (D / 32);
@@ -881,22 +990,27 @@ static hipError_t launch_pack_d(const PrefillParams& p, hipStream_t stream) {
     a.kv_heads = p.kv_heads; a.seq_k = p.seq_k; a.R = p.v_tile_rows; a.hadamard = p.hadamard;
     a.n_tiles = L.n_tiles; a.n_vtiles = L.n_vtiles; a.total_k = total_k; a.nblk_k = nblk_k;
     a.vtile = wvt; a.rec = p.ws + L.off_rec;
-    hipLaunchKernelGGL((pack_kv_kernel<D>), dim3((unsigned)(nblk_k + bk * L.n_tiles)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((pack_kv_kernel<D, BV>), dim3((unsigned)(nblk_k + bk * L.n_tiles)), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((pack_k_kernel<D>), dim3((unsigned)nblk_k), dim3(256), 0, stream, p.k, p.ks[0], p.ks[1],
+    hipLaunchKernelGGL((pack_k_kernel<D, BV>), dim3((unsigned)nblk_k), dim3(256), 0, stream, p.k, p.ks[0], p.ks[1],
                        p.ks[2], p.kv_heads, p.seq_k, L.n_tiles, p.ws + L.off_rec, total_k, p.hadamard);
     hipLaunchKernelGGL((vtile_scale_kernel<D>), dim3((unsigned)(bk * L.n_vtiles)), dim3(256), 0, stream, p.v,
                        p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_vtiles, wvt);
-    hipLaunchKernelGGL((pack_v_kernel<D, false>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v,
+    hipLaunchKernelGGL((pack_v_kernel<D, false, BV>), dim3((unsigned)(bk * L.n_tiles)), dim3(256), 0, stream, p.v,
                        p.vs[0], p.vs[1], p.vs[2], p.kv_heads, p.seq_k, p.v_tile_rows, L.n_tiles, L.n_vtiles, wvt,
                        p.ws + L.off_rec);
   }
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL, int PM>
+static void launch_attn_kernel(dim3 grid, const AttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_kernel<D, CAUSAL, PM>), grid, dim3(kWaves * 64), 0, stream, a);
+}
+
 template <int D>
 static hipError_t launch_attn_d(const PrefillParams& p, hipStream_t stream) {
-  const PrefillLayout L = prefill_layout(p.batch, p.kv_heads, p.seq_k, D, p.v_tile_rows);
+  const PrefillLayout L = prefill_layout(p.batch, p.kv_heads, p.seq_k, D, p.v_tile_rows, p.p_mode == kPBf16);
   AttnArgs a;
   a.q = p.q; a.o = p.o; a.lse = p.lse;
   a.rec = p.ws + L.off_rec;
@@ -925,19 +1039,21 @@ static hipError_t launch_attn_d(const PrefillParams& p, hipStream_t stream) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)std::min<int64_t>(items, std::max(cus, 1)));
-  if (p.causal && p.single_term)
-    hipLaunchKernelGGL((attn_kernel<D, true, true>), grid, dim3(kWaves * 64), 0, stream, a);
-  else if (p.causal)
-    hipLaunchKernelGGL((attn_kernel<D, true, false>), grid, dim3(kWaves * 64), 0, stream, a);
-  else if (p.single_term)
-    hipLaunchKernelGGL((attn_kernel<D, false, true>), grid, dim3(kWaves * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<D, false, false>), grid, dim3(kWaves * 64), 0, stream, a);
+  switch (p.p_mode * 2 + (p.causal ? 1 : 0)) {
+    case kPTwoTerm * 2: launch_attn_kernel<D, false, kPTwoTerm>(grid, a, stream); break;
+    case kPTwoTerm * 2 + 1: launch_attn_kernel<D, true, kPTwoTerm>(grid, a, stream); break;
+    case kPSingle * 2: launch_attn_kernel<D, false, kPSingle>(grid, a, stream); break;
+    case kPSingle * 2 + 1: launch_attn_kernel<D, true, kPSingle>(grid, a, stream); break;
+    case kPBf16 * 2: launch_attn_kernel<D, false, kPBf16>(grid, a, stream); break;
+    default: launch_attn_kernel<D, true, kPBf16>(grid, a, stream); break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_pack(const PrefillParams& p, hipStream_t stream) {
-  return p.head_dim == 64 ? launch_pack_d<64>(p, stream) : launch_pack_d<128>(p, stream);
+  const bool bv = p.p_mode == kPBf16;
+  if (p.head_dim == 64) return bv ? launch_pack_d<64, true>(p, stream) : launch_pack_d<64, false>(p, stream);
+  return bv ? launch_pack_d<128, true>(p, stream) : launch_pack_d<128, false>(p, stream);
 }
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t stream) {

@@ -49,6 +49,13 @@ bool valid_paging(const int32_t* block_table, int page_size, int pages_per_seq, 
   return (int64_t)page_size * pages_per_seq == cap && (reinterpret_cast<uintptr_t>(block_table) & 3) == 0;
 }
 
+// The kernel mode of a call's p_mode (QK4V8_P_DEFAULT picks the library's
+// default, QK4V8_P_DEFAULT_MODE).
+PMode prefill_mode(const qk4v8_prefill_args* a) {
+  const int m = a->p_mode == QK4V8_P_DEFAULT ? QK4V8_P_DEFAULT_MODE : a->p_mode;
+  return m == QK4V8_P_FP8_SINGLE ? kPSingle : m == QK4V8_P_BF16 ? kPBf16 : kPTwoTerm;
+}
+
 qk4v8_status validate_prefill(const qk4v8_prefill_args* a) {
   if (a == nullptr) return QK4V8_ERR_NULL;
   if (a->batch < 0 || a->q_heads < 1 || a->kv_heads < 1 || a->seq_q < 0 || a->seq_k < 0) return QK4V8_ERR_SHAPE;
@@ -60,7 +67,7 @@ qk4v8_status validate_prefill(const qk4v8_prefill_args* a) {
   if (a->causal && a->seq_q > a->seq_k) return QK4V8_ERR_SHAPE;
   if (!good_scale(a->softmax_scale)) return QK4V8_ERR_SHAPE;
   if (a->seq_q > (1 << 30) || a->seq_k > (1 << 30)) return QK4V8_ERR_SHAPE;
-  if (a->p_terms != 0 && a->p_terms != 1 && a->p_terms != 2) return QK4V8_ERR_SHAPE;
+  if (a->p_mode < QK4V8_P_DEFAULT || a->p_mode > QK4V8_P_BF16) return QK4V8_ERR_SHAPE;
   if (a->hadamard != 0 && a->hadamard != 1) return QK4V8_ERR_SHAPE;
   if (a->window < 0 || (a->window > 0 && !a->causal)) return QK4V8_ERR_SHAPE;
   return QK4V8_OK;
@@ -80,7 +87,8 @@ qk4v8_status validate_prefill_memory(const qk4v8_prefill_args* a) {
   if (a->seq_k > 1 && (a->k_stride[2] < d || a->v_stride[2] < d)) return QK4V8_ERR_STRIDE;
   if (a->q_heads > 1 && a->o_stride[1] < d) return QK4V8_ERR_STRIDE;
   if (a->workspace == nullptr || !aligned(a->workspace, kWsAlign)) return QK4V8_ERR_WORKSPACE;
-  const PrefillLayout L = prefill_layout(a->batch, a->kv_heads, a->seq_k, a->head_dim, a->v_tile_rows);
+  const PrefillLayout L =
+      prefill_layout(a->batch, a->kv_heads, a->seq_k, a->head_dim, a->v_tile_rows, prefill_mode(a) == kPBf16);
   if (a->workspace_bytes < L.total) return QK4V8_ERR_WORKSPACE;
   return QK4V8_OK;
 }
@@ -181,7 +189,7 @@ qk4v8_status qk4v8_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int3
 
 size_t qk4v8_prefill_workspace_bytes(const qk4v8_prefill_args* a) {
   if (validate_prefill(a) != QK4V8_OK) return 0;
-  return prefill_layout(a->batch, a->kv_heads, a->seq_k, a->head_dim, a->v_tile_rows).total;
+  return prefill_layout(a->batch, a->kv_heads, a->seq_k, a->head_dim, a->v_tile_rows, prefill_mode(a) == kPBf16).total;
 }
 
 }  // extern "C"
@@ -230,7 +238,7 @@ qk4v8_status run_prefill(const qk4v8_prefill_args* a, hipStream_t stream, int pa
   }
   p.batch = a->batch; p.q_heads = a->q_heads; p.kv_heads = a->kv_heads; p.seq_q = a->seq_q; p.seq_k = a->seq_k;
   p.head_dim = a->head_dim; p.v_tile_rows = a->v_tile_rows; p.causal = a->causal;
-  p.single_term = a->p_terms == 1;
+  p.p_mode = prefill_mode(a);
   p.hadamard = a->hadamard;
   p.window = a->window;
   p.softmax_scale = a->softmax_scale;

@@ -37,6 +37,14 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v2s __attribute__((ext_vector_type(2)));
 
+// Two fp32 -> two bf16 (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  const v2bf r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(<N-1>), so the
 // index can feed instruction immediates (e.g. the MFMA scale byte select).
 template <int... I, class F>
@@ -229,6 +237,15 @@ __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b, const v
 template <int FA, int FB, int OPA = 0, int OPB = 0>
 __device__ __forceinline__ v16f mfma32x32x64(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, OPA, sa, OPB, sb);
+}
+
+// v_mfma_f32_32x32x16_bf16: A (32 x 16) and B (16 x 32) as 8 bf16 per lane
+// (4 dwords: row or column lane % 32, k half lane / 32), fp32 32x32 result in
+// the same lane layout as the scaled 32x32x64 instruction.
+__device__ __forceinline__ v16f mfma32x32x16_bf16(const v4i& a, const v4i& b, const v16f& c) {
+  typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
+                                                  0);
 }
 
 // Two fp32 values -> two E4M3 bytes written into the low (HI=false) or high
@@ -481,6 +498,52 @@ __device__ __forceinline__ void softmax_tile32_single(v16f (&S)[4], float c, flo
     }
 }
 
+// BF16 variant of softmax_tile32: the probabilities feed the bf16 matrix core
+// (v_mfma_f32_32x32x16_bf16) against V widened exactly to bf16, so each
+// weight is one RNE bf16 rounding of p (8 significant bits) and needs no range
+// scale: with the lazy rescale p < 2^8, well inside bf16's exponent range.
+// P^T operand of MFMA step st (16 keys): lane (q, h) supplies elements
+// 8*(st%2) .. +7 of key block st/2, i.e. dwords P[st][0..3] hold the bf16
+// pairs of S[st/2][8*(st%2) + 2w], S[st/2][8*(st%2) + 2w + 1].
+template <int NO>
+__device__ __forceinline__ void softmax_tile32_bf16(v16f (&S)[4], float c, float& m_run, v16f (&O)[NO], v16f& L,
+                                                    v4i (&P)[8]) {
+  float m4[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    float a = fmaxf(S[kb][0], S[kb][1]), b = fmaxf(S[kb][2], S[kb][3]);
+#pragma unroll
+    for (int i = 4; i < 16; i += 4) {
+      a = fmaxf(a, fmaxf(S[kb][i], S[kb][i + 1]));
+      b = fmaxf(b, fmaxf(S[kb][i + 2], S[kb][i + 3]));
+    }
+    m4[kb] = fmaxf(a, b);
+  }
+  const float mx = max_with_lane_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+  const float tmax = mx * c;
+  const float m_new = fmaxf(m_run, tmax);
+  const bool grow = __builtin_amdgcn_ballot_w64(m_new > m_run + kLazyRescale) != 0;
+  if (__builtin_expect(grow, 0)) {
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int o = 0; o < NO; ++o) O[o] *= alpha;
+    L *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[kb][i] = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -m_use));
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int i = 8 * (st & 1) + 2 * w;
+      P[st][w] = (int)bf16x2(S[st >> 1][i], S[st >> 1][i + 1]);
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -513,12 +576,5 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Two fp32 -> two bf16 (a in the low half), round to nearest even: one
-// v_cvt_pk_bf16_f32 on gfx950.
-__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
-  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  const v2bf r = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, r);
-}
 
 }  // namespace qk4v8

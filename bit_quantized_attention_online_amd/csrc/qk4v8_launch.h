@@ -19,13 +19,21 @@ hipError_t launch_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int d
 
 // Prefill: the quantized copies of K and V live in the caller's workspace in
 // the layouts the attention kernel consumes (see prefill.hip).
+// How the probabilities enter P·V.
+enum PMode {
+  kPTwoTerm = 0,   // FP8 MFMA, two E4M3 terms per weight
+  kPSingle = 1,    // FP8 MFMA, one E4M3 term (fast mode)
+  kPBf16 = 2       // BF16 MFMA: bf16 weights against V widened exactly to bf16
+};
+
 struct PrefillLayout {
   int64_t n_tiles;        // ceil(seq_k / 128)
   int64_t n_vtiles;       // ceil(seq_k / v_tile_rows)
   int64_t rec_bytes;      // one packed K/V tile record
   size_t off_rec, off_vtile, total;
 };
-PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, int v_tile_rows);
+// bf16_v: the records hold V as bf16 values (kPBf16) instead of E4M3 codes.
+PrefillLayout prefill_layout(int batch, int kv_heads, int seq_k, int head_dim, int v_tile_rows, bool bf16_v);
 
 struct PrefillParams {
   const uint16_t* q;
@@ -35,7 +43,7 @@ struct PrefillParams {
   float* lse;
   int64_t qs[3], ks[3], vs[3], os[3];
   int batch, q_heads, kv_heads, seq_q, seq_k, head_dim, v_tile_rows, causal;
-  int single_term;           // 1: fast mode (one E4M3 term per probability)
+  int p_mode;                // PMode
   int hadamard;              // 1: Q and K rotated by the Sylvester-Hadamard H_d
   int window;                // causal sliding window (0: none)
   float softmax_scale;

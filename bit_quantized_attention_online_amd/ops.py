@@ -15,6 +15,9 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqk4v8.s
 _lib = None
 
 QK4V8_OK = 0
+# probability formats of the prefill P·V product (QK4V8_P_* of include/qk4v8.h)
+P_DEFAULT, P_FP8_SINGLE, P_FP8_TWO_TERM, P_BF16 = 0, 1, 2, 3
+P_DEFAULT_MODE = P_BF16          # what P_DEFAULT selects (QK4V8_P_DEFAULT_MODE)
 STATUS_NAMES = {0: "QK4V8_OK", 1: "QK4V8_ERR_NULL", 2: "QK4V8_ERR_SHAPE", 3: "QK4V8_ERR_STRIDE",
                 4: "QK4V8_ERR_UNSUPPORTED", 5: "QK4V8_ERR_WORKSPACE", 6: "QK4V8_ERR_HIP"}
 
@@ -38,7 +41,7 @@ class PrefillArgs(ctypes.Structure):
                 ("v_tile_rows", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("p_terms", ctypes.c_int32), ("hadamard", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("p_mode", ctypes.c_int32), ("hadamard", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -158,7 +161,7 @@ def quantize_v(v, tile_rows, stream=None):
     return codes, scales
 
 
-def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms=2, hadamard=False, window=0):
+def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_mode=P_DEFAULT, hadamard=False, window=0):
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
     a = PrefillArgs()
@@ -171,7 +174,7 @@ def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms=2
     a.batch, a.q_heads, a.kv_heads, a.seq_q, a.seq_k, a.head_dim = B, Hq, Hkv, Nq, Nk, d
     a.v_tile_rows, a.causal = v_tile_rows, int(bool(causal))
     a.softmax_scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
-    a.p_terms = p_terms
+    a.p_mode = p_mode
     a.hadamard = int(bool(hadamard))
     a.window = window
     return a
@@ -184,17 +187,18 @@ def prefill_workspace_bytes(q, k, v, causal=False, softmax_scale=None, v_tile_ro
 
 
 def attn_prefill(q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, out=None,
-                 workspace=None, stream=None, p_terms=2, hadamard=False, window=0):
+                 workspace=None, stream=None, p_mode=P_DEFAULT, hadamard=False, window=0):
     """QK4V8 prefill.  q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d] bf16 (any strides
     with unit innermost).  Returns o [B, Hq, Nq, d] bf16 (and lse fp32
-    [B, Hq, Nq] when return_lse).  p_terms=1 selects the single-term fast mode;
+    [B, Hq, Nq] when return_lse).  p_mode selects the probability format of
+    P·V (P_FP8_TWO_TERM, P_BF16, P_FP8_SINGLE = fast mode; P_DEFAULT);
     hadamard=True rotates Q and K by H_d before quantization; window=W > 0
     (causal only) keeps the W most recent keys of each row."""
     for t in (q, k, v):
         _bits16(t)
     o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-    a = _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_terms, hadamard, window)
+    a = _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_mode, hadamard, window)
     need = lib().qk4v8_prefill_workspace_bytes(ctypes.byref(a))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -208,13 +212,13 @@ class PackedPrefill:
     ``pack()`` quantizes K/V into the workspace, ``attend()`` runs the
     attention kernel from it (used to time the two halves separately)."""
 
-    def __init__(self, q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, p_terms=2,
+    def __init__(self, q, k, v, causal=False, softmax_scale=None, v_tile_rows=64, return_lse=False, p_mode=P_DEFAULT,
                  hadamard=False, window=0):
         for t in (q, k, v):
             _bits16(t)
         self.o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
         self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-        self.args = _prefill_args(q, k, v, self.o, self.lse, causal, softmax_scale, v_tile_rows, p_terms,
+        self.args = _prefill_args(q, k, v, self.o, self.lse, causal, softmax_scale, v_tile_rows, p_mode,
                                   hadamard, window)
         need = lib().qk4v8_prefill_workspace_bytes(ctypes.byref(self.args))
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

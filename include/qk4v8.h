@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define QK4V8_ABI_VERSION 7
+#define QK4V8_ABI_VERSION 8
 
 typedef enum {
   QK4V8_OK = 0,
@@ -111,6 +111,13 @@ qk4v8_status qk4v8_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int3
                               int64_t group_stride, int64_t row_stride, int32_t tile_rows,
                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
+/* Probability formats of the prefill P·V product (qk4v8_prefill_args.p_mode). */
+#define QK4V8_P_DEFAULT 0
+#define QK4V8_P_FP8_SINGLE 1
+#define QK4V8_P_FP8_TWO_TERM 2
+#define QK4V8_P_BF16 3
+#define QK4V8_P_DEFAULT_MODE QK4V8_P_BF16
+
 /*
  * Prefill attention (MpFA page §2.3, §3.3): Q and K are quantized to MXFP4 and
  * V to FP8 (per-tile E8M0 scale) inside the call, then
@@ -131,21 +138,30 @@ qk4v8_status qk4v8_quantize_v(const uint16_t* v, int64_t groups, int64_t n, int3
  *   workspace : device scratch of at least qk4v8_prefill_workspace_bytes()
  *               bytes, 256-byte aligned; it receives the call's quantized
  *               copies of K and V.  Contents on return are unspecified.
- *   p_terms   : how the probabilities enter the FP8 P·V product.
- *               0 or 2 (default): two E4M3 terms per weight, hi = E4M3(p/2^X)
- *               and lo = E4M3((p - hi*2^X) / 2^(X-4)), with one E8M0 range
- *               exponent X per query row and 128-key tile; the result meets
- *               the accuracy of exact attention on the quantized operands to
- *               about 2e-3 relative L2.
- *               1 (fast mode): one E4M3 term per weight, an integral running
- *               maximum (every rescale an exact power of two) and one E8M0
- *               range exponent per query row and aligned 32-key block (the
- *               MX block size); half the P·V matrix work and fewer vector
- *               instructions, at about 2e-2 relative L2 from exact attention.
- *               Its result is independent of the tiling: with base-2 scores
+ *   p_mode    : how the probabilities enter the P·V product (QK4V8_P_*):
+ *               QK4V8_P_FP8_TWO_TERM (2): FP8 MFMA with two E4M3 terms per
+ *               weight, hi = E4M3(p/2^X) and lo = E4M3((p - hi*2^X) / 2^(X-4)),
+ *               one E8M0 range exponent X per query row and 128-key tile;
+ *               about 2e-3 relative L2 from exact attention on the quantized
+ *               operands.
+ *               QK4V8_P_BF16 (3): bf16 weights (one RNE rounding of p) on the
+ *               bf16 matrix core against V̂ widened to bf16: V is still
+ *               quantized to E4M3 with its per-tile E8M0 scale (the same codes),
+ *               and E4M3 * 2^X fits bf16 exactly, so only the weights' rounding
+ *               differs; about 2e-3 relative L2 as well, with half the vector
+ *               instructions per score of the two-term split.
+ *               QK4V8_P_FP8_SINGLE (1, fast mode): FP8 MFMA with one E4M3 term
+ *               per weight, an integral running maximum (every rescale an exact
+ *               power of two) and one E8M0 range exponent per query row and
+ *               aligned 32-key block (the MX block size); half the P·V matrix
+ *               work, at about 2e-2 relative L2 from exact attention.  Its
+ *               result is independent of the tiling: with base-2 scores
  *               t = s*log2(e) and 32-key blocks B aligned at multiples of 32,
  *               p~_j = 2^X_B * E4M3(2^(t_j - X_B)), X_B = floor(max_B t) - 7, and
  *               o = sum_j p~_j v_j / sum_j p~_j.
+ *               QK4V8_P_DEFAULT (0): QK4V8_P_DEFAULT_MODE.
+ *               The workspace holds V in the mode's format, so a pack call and
+ *               the attention call that reads it must use the same p_mode.
  *   hadamard  : 1 rotates every Q and K row by the Sylvester-Hadamard matrix
  *               H_d (+-1 entries, H_2n = [[H_n, H_n], [H_n, -H_n]]) before its
  *               MXFP4 quantization (MpFA page §3.1: a rotation spreads outlier
@@ -175,7 +191,7 @@ typedef struct {
   float softmax_scale;
   void* workspace;
   size_t workspace_bytes;
-  int32_t p_terms;
+  int32_t p_mode;
   int32_t hadamard;
   int32_t window;
 } qk4v8_prefill_args;

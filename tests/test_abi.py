@@ -21,11 +21,36 @@ def test_header_declares_the_exported_api():
     assert _declared() == sorted(ops.EXPORTED)
 
 
+def test_peaks_library_exports_its_header():
+    from bit_quantized_attention_online_amd import peaks
+    src = open(os.path.join(ROOT, "include", "qk4v8_peaks.h")).read()
+    declared = sorted(set(re.findall(r"\b(qk4v8_peak_[a-z0-9_]+)\s*\(", src)))
+    assert declared == sorted(peaks.EXPORTED)
+    L = peaks.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    d = ctypes.c_double(0)
+    assert L.qk4v8_peak_hbm_read(None, 64, ctypes.c_void_p(4096), None) == 1
+    assert L.qk4v8_peak_hbm_read(ctypes.c_void_p(4096), 60, ctypes.c_void_p(4096), None) == 2
+    assert L.qk4v8_peak_mfma(3, 10, ctypes.c_void_p(4096), ctypes.byref(d), None) == 2
+    assert L.qk4v8_peak_mfma(4, 0, ctypes.c_void_p(4096), ctypes.byref(d), None) == 2
+    assert L.qk4v8_peak_exp2(1 << 25, ctypes.c_void_p(4096), ctypes.byref(d), None) == 2
+
+
+def test_default_p_mode_matches_header():
+    src = open(os.path.join(ROOT, "include", "qk4v8.h")).read()
+    names = dict(re.findall(r"#define (QK4V8_P_[A-Z0-9_]+) (\w+)", src))
+    value = lambda n: int(names[n]) if names[n].isdigit() else value(names[n])
+    assert value("QK4V8_P_DEFAULT_MODE") == ops.P_DEFAULT_MODE
+    assert [value(n) for n in ("QK4V8_P_DEFAULT", "QK4V8_P_FP8_SINGLE", "QK4V8_P_FP8_TWO_TERM", "QK4V8_P_BF16")] == \
+        [ops.P_DEFAULT, ops.P_FP8_SINGLE, ops.P_FP8_TWO_TERM, ops.P_BF16]
+
+
 def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.qk4v8_abi_version() == 7
+    assert L.qk4v8_abi_version() == 8
     for s in range(7):
         assert L.qk4v8_status_string(s)
 
@@ -67,7 +92,7 @@ def _prefill(**kw):
     (dict(causal=2), 2), (dict(seq_q=65), 2), (dict(softmax_scale=0.0), 2), (dict(softmax_scale=float("nan")), 2),
     (dict(q=None), 1), (dict(q_stride=[64 * 128, 128, 36]), 3), (dict(o_stride=[64 * 128, 128, 4]), 3),
     (dict(k=4100), 3), (dict(workspace=None), 5), (dict(workspace=1 << 20 | 8), 5), (dict(workspace_bytes=16), 5),
-    (dict(p_terms=3), 2), (dict(hadamard=2), 2), (dict(window=-1), 2), (dict(window=16, causal=0), 2),
+    (dict(p_mode=4), 2), (dict(p_mode=-1), 2), (dict(hadamard=2), 2), (dict(window=-1), 2), (dict(window=16, causal=0), 2),
 ])
 def test_prefill_validation(kw, status):
     a = _prefill(**kw)

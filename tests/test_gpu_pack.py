@@ -34,12 +34,13 @@ def block_key(kb, rho):
     return 32 * kb + 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3)
 
 
-def unpack_records(ws, bk, seq_k, d):
+def unpack_records(ws, bk, seq_k, d, bf16_v=False):
     """Workspace bytes -> (k_codes [bk, T*128, d/2], k_scales [bk, T*128, d/32],
-    v_codes [bk, T*128, d], v_scale_words [bk, T, 4])."""
+    v_codes [bk, T*128, d] (bf16_v: V values as bf16 bits, uint16), v_scale_words
+    [bk, T, 4])."""
     NS = d // 64
     K, SC = 4 * NS * 1024, 1024
-    REC = K + SC + 128 * d
+    REC = K + SC + 128 * d * (2 if bf16_v else 1)
     T = -(-seq_k // 128)
     rec = ws[:bk * T * REC].reshape(bk, T, REC)
     kc = np.zeros((bk, T, 128, d // 2), np.uint8)
@@ -52,6 +53,17 @@ def unpack_records(ws, bk, seq_k, d):
                 off = (kb * NS + step) * 1024 + lane * 16
                 kc[:, :, kk, 16 * g:16 * g + 16] = rec[:, :, off:off + 16]
                 ks[:, :, kk, g] = rec[:, :, K + lane * 4 * NS + kb * NS + step]
+    if bf16_v:
+        # [db][st][lane][8 bf16]: column 32 db + lane % 32, keys
+        # 32 (st // 2) + 16 (lane // 32) + 8 (st % 2) .. +7
+        vb = np.zeros((bk, T, 128, d), np.uint16)
+        words = rec[:, :, K + SC:].copy().view(np.uint16).reshape(bk, T, d * 16, 8)
+        for o in range(d * 16):
+            lane, st, db = o & 63, (o >> 6) & 7, o >> 9
+            col, k0 = db * 32 + (lane & 31), 32 * (st >> 1) + 16 * (lane >> 5) + 8 * (st & 1)
+            vb[:, :, k0:k0 + 8, col] = words[:, :, o]
+        vsw = rec[:, :, K + 512:K + 516]
+        return kc.reshape(bk, T * 128, -1), ks.reshape(bk, T * 128, -1), vb.reshape(bk, T * 128, d), vsw
     vc = np.zeros((bk, T, 128, d), np.uint8)
     for o in range(d * 8):
         lane, half, s2, db = o & 63, (o >> 6) & 1, (o >> 7) & 1, o >> 8
@@ -73,27 +85,58 @@ CASES = [
     (1, 2, 257, 64, 32, True),
     (1, 1, 600, 128, 256, True),
 ]
+# (B, Hkv, seq_k, d, R, hadamard) of the bf16-V records (QK4V8_P_BF16)
+BF16_CASES = [(2, 2, 300, 128, 64, False), (1, 2, 700, 128, 256, False), (1, 3, 129, 64, 32, True)]
 
 
-@pytest.mark.parametrize("B,Hkv,seq_k,d,R,had", CASES)
-def test_pack_kv_codes_are_bit_exact(gpu, B, Hkv, seq_k, d, R, had):
-    from bit_quantized_attention_online_amd import ops
+def _pack_inputs(B, Hkv, seq_k, d, R, had):
     rng = np.random.default_rng(seq_k * 7 + d + R + int(had))
-    # K with outlier channels and a wide spread of row scales; V with tiles of
-    # very different magnitudes (so neighbouring V tiles get different scales)
     k = rng.standard_normal((B, Hkv, seq_k, d)).astype(np.float32)
     k[..., rng.choice(d, 3, replace=False)] *= 20.0
     k *= np.exp2(rng.integers(-6, 6, (B, Hkv, seq_k, 1))).astype(np.float32)
     v = (rng.standard_normal((B, Hkv, seq_k, d))
          * np.exp2(rng.integers(-8, 8, (B, Hkv, seq_k // 16 + 1, 1)).repeat(16, axis=2)[:, :, :seq_k])
          ).astype(np.float32)
-    kb, vb = synth.bf16_bits(k), synth.bf16_bits(v)
+    return synth.bf16_bits(k), synth.bf16_bits(v)
+
+
+@pytest.mark.parametrize("B,Hkv,seq_k,d,R,had", BF16_CASES)
+def test_pack_kv_bf16_values_are_the_fp8_quantization(gpu, B, Hkv, seq_k, d, R, had):
+    """bf16 mode: the records' V values are exactly the E4M3 codes times the
+    tile scale of the oracle's FP8 quantization, and the K codes are bit-exact."""
+    from bit_quantized_attention_online_amd import ops
+    kb, vb = _pack_inputs(B, Hkv, seq_k, d, R, had)
+    print(f"[case] pack_kv bf16 V B{B} Hkv{Hkv} seq_k{seq_k} d{d} R{R} hadamard={had}", flush=True)
+    q = torch.zeros((B, Hkv, 1, d), dtype=torch.bfloat16, device="cuda")
+    pp = ops.PackedPrefill(q, to_dev(kb), to_dev(vb), causal=False, v_tile_rows=R, hadamard=had, p_mode=3)
+    pp.workspace.fill_(0xA5)
+    pp.pack()
+    torch.cuda.synchronize()
+    bk = B * Hkv
+    kc, ks, vbits, _ = unpack_records(pp.workspace.cpu().numpy(), bk, seq_k, d, bf16_v=True)
+    rkc, rks = (quant.quantize_qk_hadamard(kb) if had else quant.quantize_qk(kb))
+    rvc, rvs = quant.quantize_v(vb.reshape(bk, seq_k, d), R)
+    vhat = quant.dequantize_v(rvc, rvs, R).astype(np.float32)          # exact in float32
+    vhat_bits = vhat.view(np.uint32)
+    assert not (vhat_bits & 0xFFFF).any()                               # and in bf16
+    assert np.array_equal(kc[:, :seq_k], rkc.reshape(bk, seq_k, -1))
+    assert np.array_equal(ks[:, :seq_k], rks.reshape(bk, seq_k, -1))
+    assert np.array_equal(vbits[:, :seq_k], (vhat_bits >> 16).astype(np.uint16))
+    assert not vbits[:, seq_k:].any()
+
+
+@pytest.mark.parametrize("B,Hkv,seq_k,d,R,had", CASES)
+def test_pack_kv_codes_are_bit_exact(gpu, B, Hkv, seq_k, d, R, had):
+    from bit_quantized_attention_online_amd import ops
+    # K with outlier channels and a wide spread of row scales; V with tiles of
+    # very different magnitudes (so neighbouring V tiles get different scales)
+    kb, vb = _pack_inputs(B, Hkv, seq_k, d, R, had)
     print(f"[case] pack_kv B{B} Hkv{Hkv} seq_k{seq_k} d{d} R{R} hadamard={had}", flush=True)
     # K stored token-major ([B, N, H, d] viewed as [B, H, N, d]): strided rows
     kd = to_dev(np.ascontiguousarray(kb.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
     vd = to_dev(vb)
     q = torch.zeros((B, Hkv, 1, d), dtype=torch.bfloat16, device="cuda")
-    pp = ops.PackedPrefill(q, kd, vd, causal=False, v_tile_rows=R, hadamard=had)
+    pp = ops.PackedPrefill(q, kd, vd, causal=False, v_tile_rows=R, hadamard=had, p_mode=ops.P_FP8_TWO_TERM)
     pp.workspace.fill_(0xA5)              # bytes the pack must overwrite
     pp.pack()
     torch.cuda.synchronize()

@@ -20,13 +20,13 @@ def _inputs(B, Hq, Hkv, Nq, Nk, d, seed, k_scale=1.0):
     return q, k, v
 
 
-def _run(q, k, v, causal, R, scale=None, lse=True):
+def _run(q, k, v, causal, R, scale=None, lse=True, p_mode=0):
     from bit_quantized_attention_online_amd import ops
     d = q.shape[-1]
     scale = scale if scale is not None else 1.0 / math.sqrt(d)
-    print(f"[case] prefill q{q.shape} k{k.shape} causal={causal} R={R}", flush=True)
+    print(f"[case] prefill q{q.shape} k{k.shape} causal={causal} R={R} p_mode={p_mode}", flush=True)
     o, l = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=causal, softmax_scale=scale, v_tile_rows=R,
-                            return_lse=True)
+                            return_lse=True, p_mode=p_mode)
     torch.cuda.synchronize()
     ro, rl = oatt.qk4v8_prefill(q, k, v, scale, causal, R)
     return from_dev_bf16(o), l.cpu().numpy().astype(np.float64), ro, rl
@@ -44,12 +44,19 @@ CASES = [
 ]
 
 
+# the probability formats of the default bar (5e-3 relative L2): two-term FP8
+# and bf16 (QK4V8_P_FP8_TWO_TERM, QK4V8_P_BF16)
+P_MODES = [2, 3]
+
+
+@pytest.mark.parametrize("p_mode", P_MODES)
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,R", CASES)
-def test_prefill_parity(gpu, B, Hq, Hkv, Nq, Nk, d, causal, R):
+def test_prefill_parity(gpu, B, Hq, Hkv, Nq, Nk, d, causal, R, p_mode):
     q, k, v = _inputs(B, Hq, Hkv, Nq, Nk, d, seed=B * 1000 + Nq + Nk + d)
-    o, l, ro, rl = _run(q, k, v, causal, R)
-    assert_attn_close(o, ro, f"prefill {B},{Hq},{Hkv},{Nq},{Nk},{d},{causal},{R}")
-    assert np.abs(l - rl).max() < 5e-3    # normalizer = sum of the two-term FP8 weights (rel. error <= 2^-8)
+    o, l, ro, rl = _run(q, k, v, causal, R, p_mode=p_mode)
+    assert_attn_close(o, ro, f"prefill {B},{Hq},{Hkv},{Nq},{Nk},{d},{causal},{R} p_mode={p_mode}")
+    # normalizer = sum of the quantized weights (two-term FP8: rel. error <= 2^-8 each; bf16: <= 2^-9)
+    assert np.abs(l - rl).max() < 5e-3
 
 
 def test_prefill_tiny_workload(gpu):
@@ -88,18 +95,22 @@ def test_prefill_strided_layouts_and_determinism(gpu):
 @pytest.mark.timeout(600)
 def test_prefill_causal_gqa_workload_full(gpu):
     """The causal GQA prefill workload at full size (B4 Hq32 Hkv8 N4096 d128,
-    4 outlier K channels x20), every output compared with the oracle."""
+    4 outlier K channels x20), every output of both default-bar probability
+    formats compared with the oracle."""
     w = synth.WORKLOADS[2]
     q, k, v = synth.prefill_inputs(2)
     from bit_quantized_attention_online_amd import ops
-    print("[case] full causal GQA workload", flush=True)
-    o = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=True, softmax_scale=1 / math.sqrt(128),
-                         v_tile_rows=w["v_tile_rows"])
-    torch.cuda.synchronize()
-    o = from_dev_bf16(o)
+    outs = {}
+    for pm in P_MODES:
+        print(f"[case] full causal GQA workload p_mode={pm}", flush=True)
+        o = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=True, softmax_scale=1 / math.sqrt(128),
+                             v_tile_rows=w["v_tile_rows"], p_mode=pm)
+        torch.cuda.synchronize()
+        outs[pm] = from_dev_bf16(o)
     for b in range(w["B"]):
         ro, _ = oatt.qk4v8_prefill(q[b:b + 1], k[b:b + 1], v[b:b + 1], 1 / math.sqrt(128), True, 64)
-        assert_attn_close(o[b:b + 1], ro, f"workload 2 batch {b}")
+        for pm in P_MODES:
+            assert_attn_close(outs[pm][b:b + 1], ro, f"workload 2 batch {b} p_mode={pm}")
 
 
 @pytest.mark.timeout(600)
@@ -113,15 +124,17 @@ def test_prefill_long_causal_workload_sampled_rows(gpu):
     q = synth.normal_tensor(4, synth.Q_ID, 1, 64, N, 128)
     k = np.stack([synth.prefill_k_slice(4, w, 0, h) for h in range(8)])[None]
     v = synth.normal_tensor(4, synth.V_ID, 1, 8, N, 128)
-    print("[case] long causal workload N=131072", flush=True)
-    o = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=True, softmax_scale=1 / math.sqrt(128),
-                         v_tile_rows=64)
-    torch.cuda.synchronize()
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 65536, N - 1],
                                      np.random.default_rng(4).integers(0, N, 9)]))
-    o_rows = from_dev_bf16(o[:, :, torch.from_numpy(rows).cuda()])
     ro, _ = oatt.qk4v8_prefill(q[:, :, rows], k, v, 1 / math.sqrt(128), True, 64, rows=(rows, N))
-    assert_attn_close(o_rows, ro, "workload 4 sampled rows")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    for pm in P_MODES:
+        print(f"[case] long causal workload N=131072 p_mode={pm}", flush=True)
+        o = ops.attn_prefill(qd, kd, vd, causal=True, softmax_scale=1 / math.sqrt(128), v_tile_rows=64, p_mode=pm)
+        torch.cuda.synchronize()
+        o_rows = from_dev_bf16(o[:, :, torch.from_numpy(rows).cuda()])
+        del o
+        assert_attn_close(o_rows, ro, f"workload 4 sampled rows p_mode={pm}")
 
 
 FAST_CASES = [
@@ -150,7 +163,7 @@ def test_prefill_fast_mode(gpu, B, Hq, Hkv, Nq, Nk, d, causal, R):
     scale = 1.0 / math.sqrt(d)
     print(f"[case] prefill fast q{q.shape} k{k.shape} causal={causal} R={R}", flush=True)
     o, l = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=causal, softmax_scale=scale, v_tile_rows=R,
-                            return_lse=True, p_terms=1)
+                            return_lse=True, p_mode=1)
     torch.cuda.synchronize()
     ro, rl = oatt.qk4v8_prefill_fast(q, k, v, scale, causal, R)
     got = from_dev_bf16(o)
@@ -169,7 +182,7 @@ def test_prefill_fast_mode_workload_sample(gpu):
     q, k, v = synth.prefill_inputs(2)
     scale = 1.0 / math.sqrt(w["d"])
     o = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=True, softmax_scale=scale,
-                         v_tile_rows=w["v_tile_rows"], p_terms=1)
+                         v_tile_rows=w["v_tile_rows"], p_mode=1)
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([np.arange(0, w["Nq"], 97), [w["Nq"] - 1]]))
     ro, _ = oatt.qk4v8_prefill_fast(q[:1, :, rows], k[:1], v[:1], scale, True, w["v_tile_rows"],

@@ -23,7 +23,7 @@ def _inputs(B, Hq, Hkv, Nq, Nk, d, seed):
 
 
 PREFILL_CASES = [
-    # B, Hq, Hkv, Nq, Nk, d, R, window, p_terms
+    # B, Hq, Hkv, Nq, Nk, d, R, window, p_mode
     (1, 2, 2, 700, 700, 128, 64, 100, 2),      # MHA: 256-row workgroups, early waves see masked tiles first
     (2, 8, 1, 300, 520, 128, 32, 130, 2),      # GQA 8, bottom-right offset
     (1, 4, 2, 600, 600, 64, 64, 1, 2),         # one key per row
@@ -31,6 +31,9 @@ PREFILL_CASES = [
     (1, 2, 1, 333, 333, 128, 64, 333, 2),      # window = seq_k: plain causal
     (1, 4, 4, 513, 513, 128, 128, 300, 1),     # fast mode
     (1, 16, 2, 900, 900, 128, 64, 256, 1),
+    (1, 16, 2, 1100, 1100, 128, 256, 1024, 3), # bf16 probabilities
+    (2, 8, 1, 300, 520, 128, 32, 130, 3),
+    (1, 4, 4, 513, 513, 64, 64, 300, 3),
 ]
 
 
@@ -39,9 +42,9 @@ def test_prefill_window(gpu, B, Hq, Hkv, Nq, Nk, d, R, W, pt):
     from bit_quantized_attention_online_amd import ops
     q, k, v = _inputs(B, Hq, Hkv, Nq, Nk, d, seed=Nq * 3 + Nk + W + pt)
     scale = 1.0 / math.sqrt(d)
-    print(f"[case] prefill window={W} p_terms={pt} q{q.shape} k{k.shape} R={R}", flush=True)
+    print(f"[case] prefill window={W} p_mode={pt} q{q.shape} k{k.shape} R={R}", flush=True)
     o, l = ops.attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=True, softmax_scale=scale, v_tile_rows=R,
-                            return_lse=True, p_terms=pt, window=W)
+                            return_lse=True, p_mode=pt, window=W)
     torch.cuda.synchronize()
     ref = oatt.qk4v8_prefill_fast if pt == 1 else oatt.qk4v8_prefill
     ro, rl = ref(q, k, v, scale, True, R, window=W)
