@@ -10,7 +10,8 @@
 // G*q_len query rows of a KV head (G = q_heads / kv_heads) form up to four
 // 16-row blocks, one wave each; every wave streams the same 128-key tiles
 // through LDS:
-//   K codes (row-major, padded rows) -> QK^T A operand (16 B per lane),
+//   K codes (row-major, 16-byte chunks XOR-swizzled by row) -> QK^T A operand
+//   (16 B per lane),
 //   V codes (row-major, 16-byte chunks XOR-swizzled by row) -> ds_read_tr8_b64
 //   gathers 8 keys of one column per lane, which is the P·V A operand layout.
 // The next tile is fetched into registers while one computes, by buffer loads
@@ -71,13 +72,25 @@ template <int D>
 struct DecTile {
   static constexpr int NB = D / 32;             // MXFP4 blocks per key
   static constexpr int NC = D / 16;             // 16-byte V chunks per key
-  static constexpr int KRB = D / 2 + 16;        // padded K row bytes in LDS
+  static constexpr int KRB = D / 2;             // K row bytes in LDS (16-byte chunks swizzled, kswz)
   static constexpr int K = 128 * KRB;
   static constexpr int KS = 128 * 4;            // one dword of scales per key
   static constexpr int V = 128 * D;
   static constexpr int VS = 16;                 // V scales of the four 32-key groups
   static constexpr int BYTES = K + KS + V + VS;
 };
+
+// K rows in LDS: the 16-byte chunk c of key row r sits at chunk position
+// c ^ ((r / 16) % NB).  The QK^T operand read of one 16-lane group touches
+// keys K0 + 16*a + b (a, b = 0..3, subtile_key), which with any 16-byte row
+// stride share their banks across a: the XOR puts the four keys of equal b in
+// four different chunk positions, so the group covers every bank once
+// (measured without it: some 25M LDS bank-conflict cycles per block-verify
+// launch).
+template <int D>
+__device__ __forceinline__ int kswz(int row, int chunk) {
+  return chunk ^ ((row >> 4) & (DecTile<D>::NB - 1));
+}
 
 template <int D>
 __device__ __forceinline__ int vswz(int row, int chunk) {
@@ -159,6 +172,9 @@ decode_split_kernel(DecodeArgs a) {
   const v8i ones = v8i{(int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones,
                        (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones};
   const int klg = lg & (NB - 1);    // D = 64: lanes of k-blocks 2, 3 reread blocks 0, 1 (their Q is zero)
+  // swizzled position of this lane's K chunk: (key / 16) % 4 is (ql / 4) % 4
+  // for every key subtile_key(t, ql) gives, so it is the same for all t
+  const int kchunk = kswz<D>(subtile_key(0, ql), klg) * 16;
 
   // ---- tile staging: the next tile is held in registers while this one
   // computes, then written to LDS (K rows padded, V chunks XOR-swizzled).
@@ -238,7 +254,10 @@ decode_split_kernel(DecodeArgs a) {
     static_for<KPT>([&](auto I) {
       constexpr int i = decltype(I)::value;
       const int ci = tid + i * NT;
-      if (KCH % NT == 0 || ci < KCH) *reinterpret_cast<v4i*>(lk + (ci / NB) * T::KRB + (ci % NB) * 16) = rk[i];
+      if (KCH % NT == 0 || ci < KCH) {
+        const int row = ci / NB;
+        *reinterpret_cast<v4i*>(lk + row * T::KRB + kswz<D>(row, ci % NB) * 16) = rk[i];
+      }
     });
     static_for<VPT>([&](auto I) {
       constexpr int i = decltype(I)::value;
@@ -279,7 +298,7 @@ decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int key = subtile_key(t, ql);
-      const v8i af = fp4_operand(*reinterpret_cast<const uint4*>(lk + key * T::KRB + klg * 16));
+      const v8i af = fp4_operand(*reinterpret_cast<const uint4*>(lk + key * T::KRB + kchunk));
       const int sa = (int)((reinterpret_cast<const uint32_t*>(lks)[key] >> (8 * klg)) & 0xFF);
       S[t] = mfma16x16x128<kFmtFp4, kFmtFp4>(af, qf, v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc);
     }

@@ -306,6 +306,37 @@ def attn_decode(q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256
     return (o, lse) if return_lse else o
 
 
+class PreparedDecode:
+    """A decode / block-verify call whose arguments are marshalled once:
+    ``__call__`` only enqueues qk4v8_attn_decode on the stream (for loops that
+    call the same shapes and buffers repeatedly).  Same arguments as
+    ``attn_decode``; the output (and lse) tensors are ``self.o`` / ``self.lse``."""
+
+    def __init__(self, q, k_codes, k_scales, v_codes, v_scales, kv_len, v_tile_rows=256, kv_lens=None, num_splits=0,
+                 softmax_scale=None, return_lse=False, out=None, workspace=None, hadamard=False, window=0,
+                 block_table=None, page_size=0):
+        _bits16(q)
+        if kv_lens is not None and kv_lens.dtype != torch.int32:
+            raise TypeError("kv_lens must be int32")
+        self.o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+        a = _decode_args(q, k_codes, k_scales, v_codes, v_scales, self.o, self.lse, kv_len, v_tile_rows, kv_lens,
+                         num_splits, softmax_scale, block_table, page_size)
+        a.hadamard = int(bool(hadamard))
+        a.window = window
+        need = lib().qk4v8_decode_workspace_bytes(ctypes.byref(a))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        self.args, self.workspace = a, workspace
+        self._ref = ctypes.byref(a)
+        self._keep = (q, k_codes, k_scales, v_codes, v_scales, kv_lens, block_table)
+
+    def __call__(self, stream=None):
+        _check(lib().qk4v8_attn_decode(self._ref, _stream(stream)), "qk4v8_attn_decode")
+        return self.o
+
+
 def attn_decode_noalloc(q, k_codes, k_scales, v_codes, v_scales, kv_len, out, lse=None, v_tile_rows=256,
                         kv_lens=None, num_splits=0, softmax_scale=None, stream=None, hadamard=False, window=0,
                         block_table=None, page_size=0):
@@ -324,21 +355,16 @@ def attn_decode_noalloc(q, k_codes, k_scales, v_codes, v_scales, kv_len, out, ls
     return out
 
 
-def kv_append(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows=256,
-              kv_lens=None, stream=None, hadamard=False, block_table=None, page_size=0):
-    """Quantize n_new tokens per sequence into a decode cache (in place).
-    k_new, v_new [B, n_new, Hkv, d] bf16 (token-major, strided); cache tensors as
-    for attn_decode with capacity cap = k_codes.shape[2] (paged: page pools and
-    block_table / page_size as for attn_decode); v_tail [B, Hkv, R, d] bf16
-    keeps the source rows of each sequence's partial V tile.  kv_lens (device
-    int32 [B]) or kv_len: tokens already cached; not modified."""
+def _append_args(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows, kv_lens, hadamard,
+                 block_table, page_size):
+    """Checked AppendArgs for qk4v8_kv_append, or None for an empty append."""
     _bits16(k_new)
     _bits16(v_new)
     if kv_lens is not None and kv_lens.dtype != torch.int32:
         raise TypeError("kv_lens must be int32")
     B, n_new, Hkv, d = k_new.shape
     if B == 0 or n_new == 0:
-        return
+        return None
     for t in (k_new, v_new):
         if t.stride(-1) != 1:
             raise ValueError("innermost stride must be 1")
@@ -364,4 +390,34 @@ def kv_append(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len
     paged_cap = _paging(a, block_table, page_size)
     if paged_cap is not None:
         a.cap = paged_cap
-    _check(lib().qk4v8_kv_append(ctypes.byref(a), _stream(stream)), "qk4v8_kv_append")
+    return a
+
+
+def kv_append(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows=256,
+              kv_lens=None, stream=None, hadamard=False, block_table=None, page_size=0):
+    """Quantize n_new tokens per sequence into a decode cache (in place).
+    k_new, v_new [B, n_new, Hkv, d] bf16 (token-major, strided); cache tensors as
+    for attn_decode with capacity cap = k_codes.shape[2] (paged: page pools and
+    block_table / page_size as for attn_decode); v_tail [B, Hkv, R, d] bf16
+    keeps the source rows of each sequence's partial V tile.  kv_lens (device
+    int32 [B]) or kv_len: tokens already cached; not modified."""
+    a = _append_args(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows, kv_lens,
+                     hadamard, block_table, page_size)
+    if a is not None:
+        _check(lib().qk4v8_kv_append(ctypes.byref(a), _stream(stream)), "qk4v8_kv_append")
+
+
+class PreparedAppend:
+    """A cache append whose arguments are marshalled once (same arguments as
+    ``kv_append``); ``__call__`` only enqueues qk4v8_kv_append."""
+
+    def __init__(self, k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows=256,
+                 kv_lens=None, hadamard=False, block_table=None, page_size=0):
+        self.args = _append_args(k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_len, v_tile_rows,
+                                 kv_lens, hadamard, block_table, page_size)
+        self._ref = ctypes.byref(self.args) if self.args is not None else None
+        self._keep = (k_new, v_new, k_codes, k_scales, v_codes, v_scales, v_tail, kv_lens, block_table)
+
+    def __call__(self, stream=None):
+        if self._ref is not None:
+            _check(lib().qk4v8_kv_append(self._ref, _stream(stream)), "qk4v8_kv_append")
