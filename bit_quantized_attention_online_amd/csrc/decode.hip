@@ -387,16 +387,33 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const float* __restri
   const int b = (int)(bk / kv_heads), kvh = (int)(bk - (int64_t)b * kv_heads);
   const int qt = mrow / group, head = kvh * group + (mrow - qt * group);
   const float* pl = part_lse + bk * splits * M + mrow;
-  float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, pl[(int64_t)s * M]);
-  float wsum = 0.f;
+  // splits in groups of four, all eight loads of a group in flight at once
+  // (one memory round trip per group rather than one for the sums' maximum
+  // and another for the partials), merged into a running maximum; an empty
+  // split has lse -inf and a zero partial, so it adds nothing
+  float mx = -INFINITY, wsum = 0.f;
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  if (mx != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float w = __builtin_amdgcn_exp2f(pl[(int64_t)s * M] - mx);
-      wsum += w;
-      acc += w * *reinterpret_cast<const v4f*>(part_o + ((bk * splits + s) * M + mrow) * D + e);
+  for (int s0 = 0; s0 < splits; s0 += 4) {
+    float ls[4];
+    v4f po[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = s0 + k < splits ? s0 + k : splits - 1;
+      ls[k] = s0 + k < splits ? pl[(int64_t)s * M] : -INFINITY;
+      po[k] = *reinterpret_cast<const v4f*>(part_o + ((bk * splits + s) * M + mrow) * D + e);
     }
+    const float m_new = fmaxf(fmaxf(mx, fmaxf(ls[0], ls[1])), fmaxf(ls[2], ls[3]));
+    if (m_new == -INFINITY) continue;
+    const float sc = __builtin_amdgcn_exp2f(mx - m_new);   // 0 while mx is -inf
+    wsum *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float w = __builtin_amdgcn_exp2f(ls[k] - m_new);
+      wsum += w;
+      acc += w * po[k];
+    }
+    mx = m_new;
   }
   const v4f val = wsum > 0.f ? acc / wsum : v4f{0.f, 0.f, 0.f, 0.f};
   uint16_t* dst = o + b * os0 + qt * os1 + (int64_t)head * os2 + e;

@@ -34,6 +34,7 @@ DEC_CASES = [
     (2, 4, 4, 1, 300, 300, 64, 32, 0, False),
     (1, 6, 2, 3, 130, 140, 64, 128, 2, True),
     (2, 8, 8, 1, 1, 1, 128, 256, 0, False),         # a single cached token
+    (1, 8, 2, 2, 1300, 1300, 128, 256, 9, True),    # nine splits, three of them empty
 ]
 
 
