@@ -144,6 +144,7 @@ def measure_prefill(torch, pp, steps, warmup, settle_s, stream, with_pack=True):
     settle(torch, step, seconds=settle_s)
     for _ in range(warmup):
         step()
+    torch.cuda.synchronize()          # the wall clock starts with the warmup drained
     t0 = time.perf_counter()
     step_ms = time_calls(torch, step, steps, stream)
     wall = (time.perf_counter() - t0) * 1e3 / steps
@@ -390,16 +391,16 @@ def bench_append_prefill(torch, ops, synth, steps, warmup):
     return out
 
 
-def cpu_baseline(synth, kv_heads=(0, 5), rows_per_head=64):
+def cpu_baseline(synth, kv_heads=(0, 5), rows_per_head=256):
     """The oracle as it stands, timed on a bounded sample of the headline
     workload (131072-token causal prefill, 64 query / 8 KV heads) and
     extrapolated to the whole step.  The sample: two KV heads (their K/V
-    quantized in full, as the oracle's prefill does) and 64 seeded query rows
-    of each of their 16 query heads (1024 rows, rows 0 and N-1 and 128-key
+    quantized in full, as the oracle's prefill does) and 256 seeded query rows
+    of each of their 16 query heads (4096 rows, rows 0 and N-1 and 128-key
     tile edges included), each row attending to its full causal prefix.  The
     oracle's cost is K/V quantization per KV head plus, per query row, a
     product with all N keys (it masks after the product), so the full step is
-    extrapolated as 8/2 x the K/V part plus 64*N/1024 x the row part.  The row
+    extrapolated as 8/2 x the K/V part plus 64*N/4096 x the row part.  The row
     part is timed again on one BLAS thread (one query head's rows)."""
     import numpy as np
     from oracle import attention as oatt
