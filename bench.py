@@ -56,7 +56,7 @@ SETTLE_S = 0.5                 # untimed sustained load before the warmup steps
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_causal_gqa_n4096_traffic.json")
 LONG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_long_causal_n131072_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "bit_quantized_attention_online_amd", "csrc", "prefill.hip")
-DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_verify_traffic.json")
 DECODE_SOURCE = os.path.join(ROOT, "bit_quantized_attention_online_amd", "csrc", "decode.hip")
 
 

@@ -19,6 +19,11 @@
 // once).  Each split writes its normalized fp32 partial output and
 // log2-sum-exp; the merge kernel combines splits with log-sum-exp weights.
 //
+// Four row blocks at head_dim 128 (a drafted block of 8 tokens over 8 query
+// heads per KV head) run verify_pingpong_kernel instead: two 4-wave groups
+// per workgroup, one workgroup per CU, that take turns between matrix and
+// vector work, with tiles copied from global memory straight into LDS.
+//
 // Sliding window (MiMo page, section "DFlash块扩散推测解码": the drafter keeps
 // only the most recent 1024 keys): the splits cover the keys from the tile
 // holding the first query's first visible key to the end of the sequence, so
@@ -95,6 +100,115 @@ __device__ __forceinline__ int kswz(int row, int chunk) {
 template <int D>
 __device__ __forceinline__ int vswz(int row, int chunk) {
   return chunk ^ (row & (DecTile<D>::NC - 1));
+}
+
+// ---- pieces of the block-verify kernel below ----
+
+// The sequence length a workgroup sees.  A length outside [q_len, kv_len] is
+// outside the contract: above kv_len it is clamped to kv_len, so every read
+// stays inside the cache's capacity (and a paged sequence inside its
+// block-table row); below q_len the sequence is empty (zero output rows, lse
+// -inf).
+__device__ __forceinline__ int sequence_length(const DecodeArgs& a, int b) {
+  const int n = a.kv_lens ? a.kv_lens[b] : a.kv_len;
+  return n > a.kv_len ? a.kv_len : (n < a.q_len ? 0 : n);
+}
+
+// The keys [j_begin, j_end) split s covers, in ntiles 128-key tiles.  The
+// splits share a range that starts at key 0, or with a window at the tile
+// holding query 0's first visible key.
+struct SplitRange {
+  int j_begin, j_end, ntiles;
+};
+__device__ __forceinline__ SplitRange split_range(const DecodeArgs& a, int kvlen, int s) {
+  SplitRange r;
+  const int j_base = a.window > 0 ? max(0, kvlen - a.q_len + 1 - a.window) & ~127 : 0;
+  r.j_begin = j_base + s * a.tiles_per_split * 128;
+  r.j_end = min(kvlen, r.j_begin + a.tiles_per_split * 128);
+  r.ntiles = r.j_end > r.j_begin ? (r.j_end - r.j_begin + 127) / 128 : 0;
+  return r;
+}
+
+// Query row mrow = t * G + (head within the group) of a KV head: its position
+// t, head, and the keys it sees, [low, low + span] (rows past M see none).
+struct QueryRow {
+  bool ok;
+  int qt, head, low;
+  uint32_t span;
+};
+__device__ __forceinline__ QueryRow query_row(const DecodeArgs& a, int kvh, int kvlen, int mrow) {
+  QueryRow r;
+  r.ok = mrow < a.M;
+  r.qt = r.ok ? mrow / a.group : 0;
+  r.head = kvh * a.group + (r.ok ? mrow - r.qt * a.group : 0);
+  const int lim = r.ok ? kvlen - a.q_len + r.qt : -1;   // last visible key
+  r.low = !r.ok ? (1 << 30) : a.window > 0 ? max(0, lim - a.window + 1) : 0;
+  r.span = r.ok ? (uint32_t)(lim - r.low) : 0u;
+  return r;
+}
+
+// The QK^T B operand of lane (row, k-block lg): the row's MXFP4 codes of
+// head_dim block lg (zero past the row count and for lg >= NB) and their
+// E8M0 scale.  Rotated queries: lane (q, g) holds block g, so the Hadamard
+// stage across 32-element blocks pairs lanes l and l ^ 16 and the one across
+// 64-element blocks lanes l and l ^ 32.
+template <int D>
+__device__ __forceinline__ v8i query_operand(const DecodeArgs& a, int b, const QueryRow& r, int lg, int& qsc) {
+  constexpr int NB = D / 32;
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = 0;
+  if (r.ok && lg < NB) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.q + b * a.qs0 + r.qt * a.qs1 + (int64_t)r.head * a.qs2 + 32 * lg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 x = src[i];
+      w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+    }
+  }
+  uint32_t cq[4] = {0, 0, 0, 0};
+  qsc = 127;
+  if (!a.hadamard) {
+    if (r.ok && lg < NB) qsc = (int)mxfp4_quantize32(w, cq);
+  } else {
+    float x[32];
+    unpack_bf16x32(w, x);
+    fwht32(x);
+    hadamard_stage_lane_xor16(x, (lg & 1) != 0);
+    if constexpr (NB == 4) hadamard_stage_lane_xor32(x, (lg & 2) != 0);
+    if (r.ok && lg < NB) qsc = (int)mxfp4_quantize32f(x, cq);
+  }
+  return fp4_operand(make_uint4(cq[0], cq[1], cq[2], cq[3]));
+}
+
+// Split s's rows of one wave: the normalized fp32 partial and its log2-sum-
+// exp, or with one split (direct) the final bf16 output and natural-log lse,
+// as the merge would write them.  Element i of column block dd in lane
+// (row, lg) is column 16 dd + 4 lg + i.
+template <int D>
+__device__ __forceinline__ void store_split_rows(const DecodeArgs& a, const v4f (&O)[D / 16], const v4f& L, float m_run,
+                                                 int64_t bk, int s, int b, int mrow, const QueryRow& r, int lg) {
+  constexpr int ND = D / 16;
+  if (!r.ok) return;
+  const float l = L[0];
+  const bool empty = !(l > 0.0f);
+  const float inv = empty ? 0.0f : 1.0f / l;
+  if (a.direct) {
+    uint16_t* orow = a.o + b * a.os0 + r.qt * a.os1 + (int64_t)r.head * a.os2;
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) {
+      const v4f v = O[dd] * inv;
+      *reinterpret_cast<uint2*>(orow + dd * 16 + 4 * lg) = make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
+    }
+    if (a.lse != nullptr && lg == 0)
+      a.lse[((int64_t)b * a.q_len + r.qt) * a.q_heads + r.head] = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
+    return;
+  }
+  const int64_t prow = (bk * a.splits + s) * a.M + mrow;
+  float* dst = a.part_o + prow * D;
+#pragma unroll
+  for (int dd = 0; dd < ND; ++dd) *reinterpret_cast<v4f*>(dst + dd * 16 + 4 * lg) = O[dd] * inv;
+  if (lg == 0) a.part_lse[prow] = empty ? -INFINITY : (m_run + __log2f(l));
 }
 
 template <int D, int MB>
@@ -368,6 +482,344 @@ decode_split_kernel(DecodeArgs a) {
   if (lg == 0) a.part_lse[prow] = empty ? -INFINITY : (m_run + __log2f(l));
 }
 
+// ds_read_tr8_b64 through a restrict pointer: once inlined, the read carries
+// alias metadata, without which the compiler's wait-count pass assumes it may
+// alias any direct global->LDS load in flight and waits for all of them.
+__device__ __forceinline__ v2i lds_read_tr8(const uint8_t* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)p);
+}
+
+// One 16-byte (or 4-byte) piece per lane from global memory straight into
+// LDS, through a buffer resource (a load with the LDS bit): lane l copies
+// bytes voffset .. voffset + SIZE - 1 of the resource's range to lds_base +
+// SIZE * l (lds_base wave-uniform).  Lanes past the range read nothing from
+// memory.  Completion is counted in vmcnt like any other load.
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_base)), 16,
+      voffset, 0, 0, kNT);
+}
+__device__ __forceinline__ void load_to_lds4(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_base)), 4,
+      voffset, 0, 0, kNT);
+}
+
+// vmcnt(N) on gfx9: vm_cnt[3:0] | exp_cnt[6:4] | lgkm_cnt[11:8] | vm_cnt[5:4]
+// << 14, the other counters left at their maximum (no wait).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Block verify with four 16-row blocks at head_dim 128: a workgroup of two
+// 4-wave groups that walk the even and the odd tiles of the split's key range
+// in a ping-pong, one phase apart, so that in every phase one wave on each
+// SIMD issues matrix instructions while the other runs the softmax.  Tiles go
+// from global memory straight into LDS, three K and three V buffers per
+// group, so no tile passes through registers; the two groups hold the same
+// query rows and merge them through LDS at the end.
+template <int D>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+verify_pingpong_kernel(DecodeArgs a) {
+  using T = DecTile<D>;
+  constexpr int NB = T::NB, ND = D / 16;
+  static_assert(NB == 4 && D == 128, "one dword of K scales per key; 1 KB holds 16 K rows or 8 V rows");
+  constexpr int KBUF = T::K + 1024;   // K codes, then the scales (wave w's 32 keys at 256 w)
+  constexpr int VBUF = T::V + 16;     // V codes, then the four 32-key scales
+  constexpr int GRP = 3 * KBUF + 3 * VBUF;
+  constexpr int kPhaseLoads = 8;      // loads one wave issues per vector phase
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * GRP];
+
+  // the wave index through readfirstlane: known wave-uniform, so the load
+  // cursors and buffer resources stay in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;          // group 0 runs one phase ahead of group 1
+  const int rb = wave & 3;            // this wave's 16-row block
+  uint8_t* gk = lds + grp * GRP;      // K buffer i at gk + i * KBUF
+  uint8_t* gv = gk + 3 * KBUF;        // V buffer i at gv + i * VBUF
+  const int ql = lane & 15, lg = lane >> 4;
+  const int s = blockIdx.x % a.splits;
+  const int64_t bk = blockIdx.x / a.splits;
+  const int b = (int)(bk / a.kv_heads), kvh = (int)(bk - (int64_t)b * a.kv_heads);
+  const int kvlen = sequence_length(a, b);
+  const SplitRange sr = split_range(a, kvlen, s);
+  const int j_begin = sr.j_begin, j_end = sr.j_end, ntiles = sr.ntiles;
+
+  const int mrow = rb * 16 + ql;
+  const QueryRow qr = query_row(a, kvh, kvlen, mrow);
+  const bool row_ok = qr.ok;
+  const int low = qr.low;
+  const uint32_t span = qr.span;
+  int qsc;
+  const v8i qf = query_operand<D>(a, b, qr, lg, qsc);
+
+  v4f O[ND];
+#pragma unroll
+  for (int dd = 0; dd < ND; ++dd) O[dd] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4f L = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  v8i Phi = v8i{}, Plo = v8i{};
+  const v8i ones = v8i{(int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones,
+                       (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones, (int)kFp8Ones};
+  const int kchunk = kswz<D>(subtile_key(0, ql), lg) * 16;
+
+  // ---- loads: in vector phase k a group requests its tile k + 3's K and
+  // tile k + 2's V, so each has two iterations to land.  Contiguous cache:
+  // rows [bk][cap], V scales [bk][cap / R]; paged cache: rows
+  // [page][kv_head][page_size], V scales [page][kv_head][page_size / R].
+  // Resources bounded to the rows inside the sequence, so a tile past the
+  // range, or the rows of the last tile past kv_len, touch no memory.  A
+  // group's k-th tile is tile 2k + grp of the range, so its cursors step by
+  // 256 keys. ----
+  const bool paged = a.block_table != nullptr;
+  struct Cursor { int j, page, slot; };
+  auto cursor_at = [&](int j) __attribute__((always_inline)) {
+    Cursor c;
+    c.j = j;
+    c.page = paged ? j / a.page_size : 0;
+    c.slot = paged ? j - c.page * a.page_size : j;
+    return c;
+  };
+  auto advance = [&](Cursor& c) __attribute__((always_inline)) {
+    c.j += 256;
+    c.slot += 256;
+    while (paged && c.slot >= a.page_size) { c.slot -= a.page_size; ++c.page; }
+  };
+  auto locate = [&](const Cursor& c, int& rows, int64_t& row, int64_t& vs0) __attribute__((always_inline)) {
+    rows = c.j < j_end ? min(128, kvlen - c.j) : 0;
+    if (!paged) {
+      row = bk * (int64_t)a.cap + c.slot;
+      vs0 = bk * a.n_vtiles_cap;
+    } else {
+      // a scalar load through the constant address space (the table is
+      // read-only here): a vector load would be counted with the tile loads
+      // in flight, and waiting for the page id would wait for all of them
+      typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+      const int64_t page = rows > 0 ? ((const_i32_ptr)(a.block_table))[(int64_t)b * a.pages_per_seq + c.page] : 0;
+      const int64_t base = page * a.kv_heads + kvh;
+      row = base * a.page_size + c.slot;
+      vs0 = base * (a.page_size >> a.log2R);
+    }
+  };
+  Cursor kcur = cursor_at(j_begin + grp * 128), vcur = kcur;
+  // K codes: wave rb fills LDS kilobytes 2 rb and 2 rb + 1 (16 rows each);
+  // the lane writing LDS chunk position p of row r fetches chunk p ^ ((r /
+  // 16) % 4), the K-row swizzle.  K scales: lanes 0..31 of wave rb fetch the
+  // dwords of keys 32 rb .. 32 rb + 31; lanes 32..63 point past the range.
+  auto issue_k = [&](uint8_t* kb) __attribute__((always_inline)) {
+    int rows;
+    int64_t row, vs0;
+    locate(kcur, rows, row, vs0);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.kc + row * (D / 2)), (short)0, rows * (D / 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.ksc + row * NB), (short)0, rows * NB, 0x00020000);
+    static_for<2>([&](auto I) {
+      const int c = rb * 2 + decltype(I)::value;
+      load_to_lds16(rk, (uint32_t)(c * 1024 + (lane >> 2) * 64 + (((lane & 3) ^ (c & 3)) * 16)), kb + c * 1024);
+    });
+    load_to_lds4(rs, lane < 32 ? (uint32_t)((rb * 32 + lane) * 4) : 1024u, kb + T::K + rb * 256);
+    advance(kcur);
+  };
+  // V codes: wave rb fills LDS kilobytes 4 rb .. 4 rb + 3 (8 rows each);
+  // the lane writing chunk position p of row r fetches chunk p ^ (r % 8).
+  // The V scale of 32-key group lane % 4 comes into a register first (a
+  // group past the sequence takes the last row's scale).
+  auto issue_v = [&](uint8_t* vb, uint8_t& vsreg) __attribute__((always_inline)) {
+    int rows;
+    int64_t row, vs0;
+    locate(vcur, rows, row, vs0);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.vc + row * D), (short)0, rows * D, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.vsc + vs0 + (vcur.slot >> a.log2R)), (short)0, rows > 0 ? 8 : 0, 0x00020000);
+    const int vrow = (vcur.slot & ((1 << a.log2R) - 1)) + min(32 * (lane & 3), max(rows, 1) - 1);
+    vsreg = __builtin_amdgcn_raw_buffer_load_b8(rvs, vrow >> a.log2R, 0, 0);
+    static_for<4>([&](auto I) {
+      const int c = rb * 4 + decltype(I)::value;
+      load_to_lds16(rv, (uint32_t)(c * 1024 + (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) * 16)), vb + c * 1024);
+    });
+    advance(vcur);
+  };
+  // Rows of the sequence's last tile past kv_len: the loads leave them
+  // untouched or zero; they are cleared here, after this wave's loads of the
+  // tile have landed, so no stale byte (an E4M3 NaN among them) meets a zero
+  // weight in the P·V product.
+  auto clear_tail = [&](uint8_t* vb, int tile) __attribute__((always_inline)) {
+    const int rows = kvlen - (j_begin + tile * 128);
+    if (rows < 128) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ci = (tid & 255) + 256 * i;   // 16-byte chunk of the tile
+        if ((ci >> 3) >= rows) *reinterpret_cast<v4i*>(vb + ci * 16) = v4i{0, 0, 0, 0};
+      }
+    }
+  };
+
+  v4f S[8];
+  int psc = 127;
+  auto qk_tile = [&](const uint8_t* kb) __attribute__((always_inline)) {
+    const uint32_t* ks = reinterpret_cast<const uint32_t*>(kb + T::K);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int key = subtile_key(t, ql);
+      const v4i kv = *reinterpret_cast<const v4i*>(kb + key * T::KRB + kchunk);
+      const v8i af = fp4_operand(make_uint4((uint32_t)kv[0], (uint32_t)kv[1], (uint32_t)kv[2], (uint32_t)kv[3]));
+      const int sa = (int)((ks[(key >> 5) * 64 + (key & 31)] >> (8 * lg)) & 0xFF);
+      S[t] = mfma16x16x128<kFmtFp4, kFmtFp4>(af, qf, v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc);
+    }
+  };
+  auto mask_tile = [&](int it) __attribute__((always_inline)) {
+    const int j0 = j_begin + it * 128;
+    if (j0 + 127 > kvlen - a.q_len || !row_ok || (a.window > 0 && j0 < kvlen - a.window)) {
+      const int low_l = low - j0 - 16 * lg;
+      static_for<8>([&](auto TT) {
+        constexpr int t = decltype(TT)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][i] = mask_range(S[t][i], subtile_key(t, i), low_l, span);
+      });
+    }
+  };
+  // column blocks in pairs: the hi and the lo instruction of one block
+  // accumulate into the same registers, so an independent instruction
+  // between them keeps a wave alone on its SIMD from stalling
+  auto pv_tile = [&](const uint8_t* vb) __attribute__((always_inline)) {
+    const int vs = vb[T::V + lg];
+    const int src_row_in_piece = ql >> 1, src_half = ql & 1;
+    auto v_operand = [&](int dd) __attribute__((always_inline)) {
+      v8i av;
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        const int row = (pc >> 1) * 64 + 16 * lg + (pc & 1) * 8 + src_row_in_piece;
+        const int addr = row * D + vswz<D>(row, dd) * 16 + src_half * 8;
+        const v2i r = lds_read_tr8(vb + addr);
+        av[2 * pc] = r[0];
+        av[2 * pc + 1] = r[1];
+      }
+      return av;
+    };
+#pragma unroll
+    for (int dd = 0; dd < ND; dd += 2) {
+      const v8i a0 = v_operand(dd), a1 = v_operand(dd + 1);
+      O[dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(a0, Phi, O[dd], vs, psc);
+      O[dd + 1] = mfma16x16x128<kFmtFp8, kFmtFp8>(a1, Phi, O[dd + 1], vs, psc);
+      O[dd] = mfma16x16x128<kFmtFp8, kFmtFp8>(a0, Plo, O[dd], vs, psc - 4);
+      O[dd + 1] = mfma16x16x128<kFmtFp8, kFmtFp8>(a1, Plo, O[dd + 1], vs, psc - 4);
+    }
+    L = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Phi, L, 127, psc);
+    L = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Plo, L, 127, psc - 4);
+  };
+
+  // ---- the ping-pong.  Iteration k of a group: a matrix phase (the lo half
+  // of the two-term split of tile k - 1, the QK^T of tile k, the P·V of tile
+  // k - 1) and a vector phase (tile k's V scales and tail, the loads of phase
+  // k, the mask and softmax of tile k), each ended by a workgroup barrier;
+  // group 1 runs one phase behind group 0.  Tile k's K sits in K buffer k % 3
+  // and its V in V buffer k % 3: the K buffer of tile k is free once this
+  // phase's QK^T has run, the V buffer of tile k - 1 once its P·V has. ----
+  const int nk = (ntiles - grp + 1) / 2;      // this group's tiles
+  const int n_it = (ntiles + 1) / 2;          // group 0's: both groups run n_it + 1 iterations, rounded up to pairs
+  uint8_t vsr[2];                             // V scales of the tiles requested two phases back
+  issue_k(gk);                                // tile 0's K
+  issue_k(gk + KBUF);                         // "phase -2": tile 1's K, tile 0's V
+  issue_v(gv, vsr[0]);
+  issue_k(gk + 2 * KBUF);                     // "phase -1": tile 2's K, tile 1's V
+  issue_v(gv + VBUF, vsr[1]);
+  wait_loads<2 * kPhaseLoads>();              // this wave's part of tile 0's K has landed
+  phase_barrier();
+  if (grp == 1) phase_barrier();
+  v4f W[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) W[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  int b3 = 0;                                 // k % 3
+  constexpr std::integral_constant<int, 0> I0{};
+  constexpr std::integral_constant<int, 1> I1{};
+  auto iteration = [&](int k, auto SL) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SL)::value;   // k % 2
+    const int bm1 = b3 == 0 ? 2 : b3 - 1;     // (k - 1) % 3, also (k + 2) % 3
+    __builtin_amdgcn_s_setprio(1);
+    // unconditional (their results are used only when the P·V and the
+    // softmax run), so that both form one block the scheduler can
+    // interleave: the K operand reads first, then each QK^T instruction
+    // followed by an eighth of the split's vector work
+    softmax_tile_lo(W, Phi, Plo);
+    qk_tile(gk + b3 * KBUF);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    static_for<8>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+    });
+    if (k >= 1 && k - 1 < nk) pv_tile(gv + bm1 * VBUF);
+    __builtin_amdgcn_s_setprio(0);
+    // the matrix instructions are pure values to the compiler, which would
+    // sink them past the barrier into the vector phase
+    static_for<ND>([&](auto DD) { keep_in_vgprs(O[decltype(DD)::value]); });
+    keep_in_vgprs(L);
+    static_for<8>([&](auto TT) { keep_in_vgprs(S[decltype(TT)::value]); });
+    phase_barrier();
+    // the loads of phase k - 2 have landed: tile k's V (read by the next
+    // P·V) and tile k + 1's K (the next QK^T)
+    wait_loads<kPhaseLoads>();
+    uint8_t* vk = gv + b3 * VBUF;
+    vk[T::V + (lane & 3)] = vsr[sl];
+    if (k < nk) clear_tail(vk, 2 * k + grp);
+    // the next loads before the softmax (measured: 2-3% faster than after it,
+    // where the waves of a group wait for the memory pipeline at the barrier)
+    issue_k(gk + b3 * KBUF);                  // tile k + 3's K
+    issue_v(gv + bm1 * VBUF, vsr[sl]);        // tile k + 2's V
+    if (k < nk) {
+      mask_tile(2 * k + grp);
+      softmax_tile_hi<ND>(S, W, a.c, m_run, O, L, Phi, psc);
+    }
+    keep_in_vgprs(Phi);
+    static_for<8>([&](auto TT) { keep_in_vgprs(W[decltype(TT)::value]); });
+    __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): LDS writes done before the barrier
+    phase_barrier();
+    b3 = b3 == 2 ? 0 : b3 + 1;
+  };
+  // unrolled by two (the V-scale register of phase k is vsr[k % 2]), always
+  // whole pairs (an iteration past n_it does nothing but its barriers and
+  // empty loads), so the compiler knows at the back edge which loads are in
+  // flight
+  for (int k = 0; k <= n_it; k += 2) {
+    iteration(k, I0);
+    iteration(k + 1, I1);
+  }
+  wait_loads<0>();                            // the empty loads past the range still write LDS
+  if (grp == 0) phase_barrier();              // matches group 1's initial wait
+  // ---- both groups hold the same rows: group 1 hands its (m, l, O) to
+  // group 0 through LDS (every tile has been consumed) ----
+  float* xf = reinterpret_cast<float*>(lds);
+  const int idx = rb * 64 + lane;
+  if (grp == 1) {
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xf[(dd * 4 + i) * 256 + idx] = O[dd][i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xf[(ND * 4 + i) * 256 + idx] = L[i];
+    xf[(ND * 4 + 4) * 256 + idx] = m_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float m1 = xf[(ND * 4 + 4) * 256 + idx];
+  const float mm = fmaxf(m_run, m1);
+  if (mm != -INFINITY) {
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[dd][i] = O[dd][i] * a0 + xf[(dd * 4 + i) * 256 + idx] * a1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L[i] = L[i] * a0 + xf[(ND * 4 + i) * 256 + idx] * a1;
+    m_run = mm;
+  }
+
+  store_split_rows<D>(a, O, L, m_run, bk, s, b, mrow, qr, lg);
+}
+
 // Combine the splits' partials with weights 2^(lse_s - max).  A query row
 // is D/4 threads of four elements each (16-byte partial loads, one 8-byte
 // bf16 store when the output allows it); a workgroup of 256 threads covers
@@ -427,6 +879,10 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const float* __restri
     lse[((int64_t)b * q_len + qt) * q_heads + head] = wsum > 0.f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
+// Four row blocks at head_dim 128 run the ping-pong workgroup.
+template <int D, int MB>
+constexpr bool kPingPong = MB == 4 && D == 128;
+
 // Workgroups of decode_split_kernel<D, MB> the current device holds at once:
 // its CU count times the runtime's occupancy figure for the compiled kernel
 // (register and LDS use), so a different compiler, register budget or device
@@ -441,9 +897,10 @@ static int64_t decode_capacity_of(int dev) {
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&decode_split_kernel<D, MB>), MB * 64, 0) != hipSuccess)
-    return 0;
+  constexpr bool pp = kPingPong<D, MB>;
+  const void* fn = pp ? reinterpret_cast<const void*>(&verify_pingpong_kernel<128>)
+                      : reinterpret_cast<const void*>(&decode_split_kernel<D, MB>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, pp ? 512 : MB * 64, 0) != hipSuccess) return 0;
   const int64_t c = (int64_t)cus * per_cu;
   if (c > 0 && dev >= 0 && dev < kMaxDevices) cache[dev].store(c, std::memory_order_relaxed);
   return c;
@@ -509,7 +966,12 @@ static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
     case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(64), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, dim3(128), 0, stream, a); break;
     case 3: hipLaunchKernelGGL((decode_split_kernel<D, 3>), grid, dim3(192), 0, stream, a); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<D, 4>), grid, dim3(256), 0, stream, a); break;
+    default:
+      if constexpr (kPingPong<D, 4>)
+        hipLaunchKernelGGL((verify_pingpong_kernel<D>), grid, dim3(512), 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_split_kernel<D, 4>), grid, dim3(256), 0, stream, a);
+      break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct) return e;

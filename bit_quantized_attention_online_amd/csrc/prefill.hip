@@ -82,27 +82,6 @@ __device__ __forceinline__ void buffer_to_lds16(const uint8_t* base, uint32_t by
       voffset, 0, 0, 0);
 }
 
-// Workgroup barrier inside the attention loop.  The LDS data it orders comes
-// from direct loads that each wave has already waited for, and every LDS read
-// before it has been consumed, so no memory fence is needed (a fence would
-// wait for the prefetches still in flight); the empty asm statements keep the
-// compiler from moving LDS accesses across it.
-__device__ __forceinline__ void phase_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// An empty asm that reads x: the value has to be computed at this point of
-// the program, which pins pure computations (matrix instructions) in place.
-template <class T>
-__device__ __forceinline__ void keep_in_vgprs(const T& x) {
-#if __HIP_DEVICE_COMPILE__
-  asm volatile("" ::"v"(x));
-#else
-  (void)x;
-#endif
-}
 
 }  // namespace
 

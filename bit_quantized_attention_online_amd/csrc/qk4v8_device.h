@@ -228,6 +228,28 @@ __host__ __device__ constexpr int subtile_key(int t, int r) {
   return (t >> 2) * 64 + 16 * (r >> 2) + 4 * (t & 3) + (r & 3);
 }
 
+// Workgroup barrier inside a tile loop whose callers have already waited for
+// the LDS data it orders (their own direct loads or staging writes), with
+// every LDS read before it consumed, so no memory fence is needed (a fence
+// would wait for the loads still in flight); the empty asm statements keep
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// An empty asm that reads x: the value has to be computed at this point of
+// the program, which pins pure computations (matrix instructions) in place.
+template <class T>
+__device__ __forceinline__ void keep_in_vgprs(const T& x) {
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("" ::"v"(x));
+#else
+  (void)x;
+#endif
+}
+
 // Scaled MFMA wrappers.  `sa`/`sb` hold E8M0 bytes; OPA/OPB select the byte.
 template <int FA, int FB, int OPA = 0, int OPB = 0>
 __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
@@ -361,6 +383,63 @@ __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run,
   for (int t = 0; t < 8; ++t) {
     const uint32_t l = e4m3_put2<false>((uint32_t)Plo[t], S[t][0], S[t][1], 0.0625f);
     Plo[t] = (int)e4m3_put2<true>(l, S[t][2], S[t][3], 0.0625f);
+  }
+}
+
+// softmax_tile in two parts with identical arithmetic, for a schedule that
+// runs the second part elsewhere: (1) the online-softmax step and the hi
+// codes, with the weights p / 2^X left in W; (2) the residuals and lo codes.
+template <int ND>
+__device__ __forceinline__ void softmax_tile_hi(v4f (&S)[8], v4f (&W)[8], float c, float& m_run, v4f (&O)[ND],
+                                                v4f& L, v8i& Phi, int& psc) {
+  float m4[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) m4[g] = fmaxf(fmaxf(S[2 * g][0], S[2 * g][1]), fmaxf(S[2 * g][2], S[2 * g][3]));
+#pragma unroll
+  for (int g = 0; g < 4; ++g) m4[g] = fmaxf(m4[g], fmaxf(fmaxf(S[2 * g + 1][0], S[2 * g + 1][1]),
+                                                       fmaxf(S[2 * g + 1][2], S[2 * g + 1][3])));
+  float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+  mx = max_with_lane_xor16(mx);
+  mx = max_with_lane_xor32(mx);
+  const float tmax = mx * c;
+  const float m_new = fmaxf(m_run, tmax);
+  const bool grow = __builtin_amdgcn_ballot_w64(m_new > m_run + kLazyRescale) != 0;
+  if (__builtin_expect(grow, 0)) {
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) O[dd] *= alpha;
+    L *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+  const int X = (int)floorf(fmaxf(tmax - m_use, -100.0f)) - 7;
+  psc = X + 127;
+  const float mX = m_use + (float)X;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) W[t][i] = __builtin_amdgcn_exp2f(fmaf(S[t][i], c, -mX));
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t h = e4m3_put2_unscaled<false>((uint32_t)Phi[t], W[t][0], W[t][1]);
+    Phi[t] = (int)e4m3_put2_unscaled<true>(h, W[t][2], W[t][3]);
+  }
+}
+
+__device__ __forceinline__ void softmax_tile_lo(v4f (&W)[8], const v8i& Phi, v8i& Plo) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const auto b01 = __builtin_amdgcn_cvt_pk_f32_fp8(Phi[t], false);
+    const auto b23 = __builtin_amdgcn_cvt_pk_f32_fp8(Phi[t], true);
+    W[t][0] -= b01[0];
+    W[t][1] -= b01[1];
+    W[t][2] -= b23[0];
+    W[t][3] -= b23[1];
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t l = e4m3_put2<false>((uint32_t)Plo[t], W[t][0], W[t][1], 0.0625f);
+    Plo[t] = (int)e4m3_put2<true>(l, W[t][2], W[t][3], 0.0625f);
   }
 }
 

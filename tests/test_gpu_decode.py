@@ -35,6 +35,11 @@ DEC_CASES = [
     (1, 6, 2, 3, 130, 140, 64, 128, 2, True),
     (2, 8, 8, 1, 1, 1, 128, 256, 0, False),         # a single cached token
     (1, 8, 2, 2, 1300, 1300, 128, 256, 9, True),    # nine splits, three of them empty
+    # four 16-row blocks at head_dim 128: the ping-pong workgroup
+    (2, 64, 8, 8, 700, 760, 128, 32, 0, True),      # ragged lengths, 32-row V tiles
+    (1, 56, 8, 8, 2100, 2200, 128, 64, 3, True),    # 56 rows, three splits
+    (2, 32, 4, 8, 100, 128, 128, 256, 0, True),     # one partial tile per sequence
+    (1, 64, 8, 8, 1300, 1300, 128, 128, 9, True),   # nine splits, some of them empty
 ]
 
 
@@ -159,7 +164,7 @@ def test_decode_workloads_full_size_sampled(gpu, cfg):
         assert np.array_equal(from_dev_bf16(op), o), "paged decode differs from the contiguous cache"
 
 
-@pytest.mark.parametrize("q_len,d", [(1, 128), (4, 128), (2, 64)])
+@pytest.mark.parametrize("q_len,d", [(1, 128), (4, 128), (16, 128), (2, 64)])
 def test_decode_hadamard(gpu, q_len, d):
     """Decode over a cache written with rotated K rows, queries rotated in the
     kernel, against the oracle's rotated definition."""
@@ -306,9 +311,9 @@ def test_decode_out_of_contract_lengths_stay_in_bounds(gpu, splits, paged):
 def test_decode_auto_split_count_on_mi355x(gpu):
     """num_splits = 0 derives the count from the CU count and the split
     kernel's occupancy; on MI355X (256 CUs) that gives 2 splits for the
-    decode workload and 3 for block verify."""
+    decode workload and 1 for block verify (one ping-pong workgroup per CU)."""
     from bit_quantized_attention_online_amd import ops
-    for cfg, want in ((3, 2), (5, 3)):
+    for cfg, want in ((3, 2), (5, 1)):
         w = synth.WORKLOADS[cfg]
         q = torch.empty((w["B"], w["q_len"], w["Hq"], w["d"]), dtype=torch.bfloat16, device="cuda")
         kc = torch.empty((w["B"], w["Hkv"], w["kv_len"], w["d"] // 2), dtype=torch.uint8, device="cuda")

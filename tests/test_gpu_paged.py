@@ -41,6 +41,7 @@ DEC_CASES = [
     (2, 16, 2, 4, 128, 64, 128, 8, True, 200),
     (2, 64, 8, 8, 128, 256, 512, 3, False, 0),
     (2, 4, 4, 1, 64, 32, 128, 6, True, 0),
+    (2, 64, 8, 8, 128, 64, 128, 9, True, 300),       # ping-pong workgroup, 128-key pages
 ]
 
 

@@ -91,6 +91,7 @@ DECODE_CASES = [
     (2, 16, 2, 4, 300, 300, 128, 128, 0, False, 2),        # window shorter than the block
     (3, 8, 2, 2, 5000, 5000, 128, 128, 0, True, 1024),
     (2, 8, 2, 1, 640, 640, 128, 256, 2, False, 640),       # window = kv_len: plain decode
+    (2, 64, 8, 8, 2000, 2100, 128, 64, 2, True, 500),      # ping-pong workgroup, two splits
 ]
 
 
