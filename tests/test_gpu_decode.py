@@ -255,21 +255,23 @@ def test_decode_ignores_cache_bytes_past_each_length(gpu, q_len, d, R):
     assert_attn_close(out, ro, "decode past-length NaN bytes")
 
 
-@pytest.mark.parametrize("splits,paged", [(0, False), (3, False), (1, False), (2, True)])
-def test_decode_out_of_contract_lengths_stay_in_bounds(gpu, splits, paged):
+@pytest.mark.parametrize("splits,paged,Hq", [(0, False, 8), (3, False, 8), (1, False, 8), (2, True, 8),
+                                             (0, False, 32), (3, False, 32), (2, True, 32)])
+def test_decode_out_of_contract_lengths_stay_in_bounds(gpu, splits, paged, Hq):
     """kv_lens above kv_len are read as kv_len, below q_len as an empty
     sequence (zero rows, lse -inf).  The cache bytes past kv_len are E4M3 NaN
     patterns, and cap is larger than every length, so a read past kv_len
-    would show as NaN in the output while staying inside the allocation."""
+    would show as NaN in the output while staying inside the allocation.
+    Hq 32 gives 64 query rows per KV head, the block-verify kernel."""
     from bit_quantized_attention_online_amd import ops
-    B, Hq, Hkv, q_len, kv_len, cap, d, R = 4, 8, 2, 4, 600, 1024, 128, 256
+    B, Hkv, q_len, kv_len, cap, d, R = 4, 2, 4, 600, 1024, 128, 256
     lens = np.array([900, 0, 3, 450], dtype=np.int32)
     clamped = np.array([600, 0, 0, 450])
     rng = np.random.default_rng(77)
     k = synth.bf16_bits(rng.standard_normal((B, Hkv, cap, d)).astype(np.float32))
     v = synth.bf16_bits(rng.standard_normal((B, Hkv, cap, d)).astype(np.float32))
     q = synth.bf16_bits(rng.standard_normal((B, q_len, Hq, d)).astype(np.float32))
-    print(f"[case] decode out-of-contract lengths {lens.tolist()} splits={splits} paged={paged}", flush=True)
+    print(f"[case] decode out-of-contract lengths {lens.tolist()} splits={splits} paged={paged} Hq={Hq}", flush=True)
     rkc, rks = quant.quantize_qk(k)
     rvc, rvs = quant.quantize_v(v.reshape(B * Hkv, cap, d), R)
     rvc, rvs = rvc.reshape(B, Hkv, cap, d), rvs.reshape(B, Hkv, -1)
