@@ -243,8 +243,11 @@ qk4v8_status qk4v8_attn_prefill_packed(const qk4v8_prefill_args* a, hipStream_t 
  *   1 <= q_len <= kv_len <= cap; (q_heads / kv_heads) * q_len <= 64.
  *   num_splits: KV splits per (batch, kv-head), 0 = chosen by the library
  *              from the current device (one round of resident workgroups:
- *              CU count times the split kernel's occupancy, at least 8
- *              tiles of 128 keys per split); with 0 the workspace query and
+ *              CU count times the occupancy of the kernel that runs, at
+ *              least 8 tiles of 128 keys per split; on MI355X 2 splits for
+ *              decode at 32768 keys and 1 for a block of 64 query rows per
+ *              KV head at head_dim 128, whose kernel holds one workgroup per
+ *              CU); with 0 the workspace query and
  *              the call return 0 / QK4V8_ERR_HIP when no device answers.
  *   workspace : at least qk4v8_decode_workspace_bytes() bytes, 256-byte aligned
  *               (fp32 partial outputs and log-sum-exps of the splits; with a
