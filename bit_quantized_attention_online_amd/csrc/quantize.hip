@@ -14,42 +14,65 @@ namespace qk4v8 {
 // One lane per 8 consecutive elements; 4 adjacent lanes own one 32-element
 // block and combine their maxima with two xor-shuffles.  Loads are 16 B per
 // lane and the code stores 4 B per lane, both contiguous across the wave.
+// Each thread takes CPT such chunks a grid apart, all loads issued before
+// any encode, so a wave keeps CPT KB of reads in flight.
+// cpr_shift: log2 of the chunks per row when that is a power of two (a
+// shift instead of a 64-bit division), else -1.
+template <int CPT>
 __global__ void __launch_bounds__(256) quantize_qk_kernel(const uint16_t* __restrict__ x, int64_t rows, int d,
                                                           int64_t ld, uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales) {
+                                                          uint8_t* __restrict__ scales, int cpr_shift) {
   const int64_t chunks_per_row = d >> 3;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  auto row_of = [&](int64_t idx) __attribute__((always_inline)) {
+    return cpr_shift >= 0 ? idx >> cpr_shift : idx / chunks_per_row;
+  };
   const int64_t total = rows * chunks_per_row;
-  const bool live = idx < total;
-  const int64_t row = live ? idx / chunks_per_row : 0;
-  const int chunk = live ? (int)(idx - row * chunks_per_row) : 0;
-  uint4 w = make_uint4(0, 0, 0, 0);
-  if (live) w = *reinterpret_cast<const uint4*>(x + row * ld + chunk * 8);
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  float amax = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t idx0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint4 w[CPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(ws[i])), fabsf(bf16_hi(ws[i]))));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-  const int X = mx_shared_exp(amax, 2);
-  uint32_t c = 0;
-  if (X >= -120) {
-    // the bf16 pairs straight through the scaled convert (x / 2^X), as in
-    // mxfp4_quantize32
-    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-    const float scale = exp2i(X);
-    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[0]), scale, 0);
-    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[1]), scale, 1);
-    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[2]), scale, 2);
-    c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[3]), scale, 3);
-  } else {
-    const float inv = exp2i(-X);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c |= e2m1_pack2(bf16_lo(ws[i]) * inv, bf16_hi(ws[i]) * inv) << (8 * i);
+  for (int i = 0; i < CPT; ++i) {
+    const int64_t idx = idx0 + i * stride;
+    w[i] = make_uint4(0, 0, 0, 0);
+    if (idx < total) {
+      const int64_t row = row_of(idx);
+      w[i] = *reinterpret_cast<const uint4*>(x + row * ld + (idx - row * chunks_per_row) * 8);
+    }
   }
-  if (live) {
-    *reinterpret_cast<uint32_t*>(codes + row * (d >> 1) + chunk * 4) = c;
-    if ((chunk & 3) == 0) scales[row * (d >> 5) + (chunk >> 2)] = (uint8_t)(X + 127);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    // a group of 4 lanes is all inside or all past the end (total is a
+    // multiple of 4 chunks), so the shuffles below stay within live groups
+    const int64_t idx = idx0 + i * stride;
+    const bool live = idx < total;
+    const int64_t row = live ? row_of(idx) : 0;
+    const int chunk = live ? (int)(idx - row * chunks_per_row) : 0;
+    const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(ws[k])), fabsf(bf16_hi(ws[k]))));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int X = mx_shared_exp(amax, 2);
+    uint32_t c = 0;
+    if (X >= -120) {
+      // the bf16 pairs straight through the scaled convert (x / 2^X), as in
+      // mxfp4_quantize32
+      typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+      const float scale = exp2i(X);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[0]), scale, 0);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[1]), scale, 1);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[2]), scale, 2);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, ws[3]), scale, 3);
+    } else {
+      const float inv = exp2i(-X);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c |= e2m1_pack2(bf16_lo(ws[k]) * inv, bf16_hi(ws[k]) * inv) << (8 * k);
+    }
+    if (live) {
+      *reinterpret_cast<uint32_t*>(codes + row * (d >> 1) + chunk * 4) = c;
+      if ((chunk & 3) == 0) scales[row * (d >> 5) + (chunk >> 2)] = (uint8_t)(X + 127);
+    }
   }
 }
 
@@ -127,9 +150,13 @@ __global__ void __launch_bounds__(256) quantize_v_kernel_2pass(const uint16_t* _
 
 hipError_t launch_quantize_qk(const uint16_t* x, int64_t rows, int d, int64_t ld, uint8_t* codes, uint8_t* scales,
                               hipStream_t stream) {
+  constexpr int kCpt = 4;   // chunks per thread
   const int64_t total = rows * (d >> 3);
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(quantize_qk_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, d, ld, codes, scales);
+  const int64_t blocks = (total + 256 * kCpt - 1) / (256 * kCpt);
+  const int cpr = d >> 3;
+  const int cpr_shift = (cpr & (cpr - 1)) == 0 ? __builtin_ctz((unsigned)cpr) : -1;
+  hipLaunchKernelGGL((quantize_qk_kernel<kCpt>), dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, d, ld, codes,
+                     scales, cpr_shift);
   return hipGetLastError();
 }
 

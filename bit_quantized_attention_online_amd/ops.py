@@ -161,6 +161,50 @@ def quantize_v(v, tile_rows, stream=None):
     return codes, scales
 
 
+class PreparedQuantizeQK:
+    """``quantize_qk`` with its output tensors allocated and its arguments
+    marshalled once; ``__call__`` only enqueues qk4v8_quantize_qk.  The
+    outputs are ``codes`` and ``scales``."""
+
+    def __init__(self, x):
+        _bits16(x)
+        d = x.shape[-1]
+        x2 = x.reshape(-1, d) if x.dim() != 2 else x
+        if x2.stride(-1) != 1:
+            raise ValueError("innermost stride must be 1")
+        rows = x2.shape[0]
+        self.codes = torch.empty(x.shape[:-1] + (d // 2,), dtype=torch.uint8, device=x.device)
+        self.scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device)
+        ld = x2.stride(0) if rows > 1 else d
+        self._args = (_ptr(x2), ctypes.c_int64(rows), ctypes.c_int32(d), ctypes.c_int64(ld), _ptr(self.codes),
+                      _ptr(self.scales))
+        self._keep = (x, x2)
+
+    def __call__(self, stream=None):
+        _check(lib().qk4v8_quantize_qk(*self._args, _stream(stream)), "qk4v8_quantize_qk")
+        return self.codes, self.scales
+
+
+class PreparedQuantizeV:
+    """``quantize_v`` with its output tensors allocated and its arguments
+    marshalled once; ``__call__`` only enqueues qk4v8_quantize_v."""
+
+    def __init__(self, v, tile_rows):
+        _bits16(v)
+        g, n, d = v.shape
+        self.codes = torch.empty((g, n, d), dtype=torch.uint8, device=v.device)
+        self.scales = torch.empty((g, -(-n // tile_rows)), dtype=torch.uint8, device=v.device)
+        gs = v.stride(0) if g > 1 else n * v.stride(1)
+        rs = v.stride(1) if n > 1 else d
+        self._args = (_ptr(v), ctypes.c_int64(g), ctypes.c_int64(n), ctypes.c_int32(d), ctypes.c_int64(gs),
+                      ctypes.c_int64(rs), ctypes.c_int32(tile_rows), _ptr(self.codes), _ptr(self.scales))
+        self._keep = v
+
+    def __call__(self, stream=None):
+        _check(lib().qk4v8_quantize_v(*self._args, _stream(stream)), "qk4v8_quantize_v")
+        return self.codes, self.scales
+
+
 def _prefill_args(q, k, v, o, lse, causal, softmax_scale, v_tile_rows, p_mode=P_DEFAULT, hadamard=False, window=0):
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape

@@ -93,3 +93,25 @@ def test_quantize_strided_views(gpu):
     c, s = ops.quantize_v(v_view, 64)
     rc, rs = quant.quantize_v(np.ascontiguousarray(x.transpose(0, 2, 1, 3)[1]), 64)
     assert np.array_equal(c.cpu().numpy(), rc) and np.array_equal(s.cpu().numpy(), rs)
+
+
+def test_prepared_quantizers_match_the_plain_calls(gpu):
+    """PreparedQuantizeQK / PreparedQuantizeV (arguments marshalled once, as
+    the bench times them) write the same bytes as quantize_qk / quantize_v."""
+    from bit_quantized_attention_online_amd import ops
+    rng = np.random.default_rng(123)
+    x = synth.bf16_bits(rng.standard_normal((3, 5, 300, 96)).astype(np.float32))
+    v = synth.bf16_bits(rng.standard_normal((6, 700, 128)).astype(np.float32))
+    xd, vd = to_dev(x), to_dev(v)
+    print("[case] prepared quantizers", flush=True)
+    c0, s0 = ops.quantize_qk(xd)
+    pq = ops.PreparedQuantizeQK(xd)
+    c1, s1 = pq()
+    c2, s2 = pq()        # a second call on the same prepared arguments
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1) and torch.equal(s0, s1) and torch.equal(c1, c2) and torch.equal(s1, s2)
+    for R in (64, 256):
+        c0, s0 = ops.quantize_v(vd, R)
+        c1, s1 = ops.PreparedQuantizeV(vd, R)()
+        torch.cuda.synchronize()
+        assert torch.equal(c0, c1) and torch.equal(s0, s1)
