@@ -679,13 +679,15 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
 
   v16f O[NDB];
-  v16f L;
+  v16f L;       // FP8 modes: row sums from the ones-operand MFMA (every row holds the sum)
+  float Lh;     // bf16 mode: this lane's share of its row's sum (the keys of its lane half)
   v16f S[4];
   float m_run;
   auto reset_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) O[db] = v16f{};
     L = v16f{};
+    Lh = 0.f;
     m_run = -INFINITY;
   };
   v8i Phi[2] = {v8i{}, v8i{}}, Plo[2] = {v8i{}, v8i{}};   // FP8 modes
@@ -711,7 +713,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const __amdgpu_buffer_rsrc_t ro =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(obase), (short)0, (int)obytes, 0x00020000);
     const uint32_t orow_off = (uint32_t)((int64_t)ql * a.os2 * 2) + 8u * lh;
-    const float l = L[0];     // every row of the ones-MFMA holds the same sum
+    const float l = BF ? sum_with_lane_xor32(Lh) : L[0];
     const float inv = 1.0f / l;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -771,7 +773,6 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         });
       };
       constexpr uint32_t kBf16Ones = 0x3F803F80u;   // two bf16 1.0
-      const v4i ones = v4i{(int)kBf16Ones, (int)kBf16Ones, (int)kBf16Ones, (int)kBf16Ones};
       bvload(std::integral_constant<int, 0>{});
       static_for<2 * NDB + 1>([&](auto J) {
         constexpr int u = decltype(J)::value;
@@ -785,8 +786,25 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
             O[db] = mfma32x32x16_bf16(bv[u & 1][j], Pb[h4 + j], O[db]);
           });
         } else {
-          // row sums of the bf16 weights: 1·P^T
-          static_for<8>([&](auto ST) { L = mfma32x32x16_bf16(ones, Pb[decltype(ST)::value], L); });
+          // row sums of the bf16 weights on the vector unit, two weights per
+          // v_dot2_f32_bf16 against (1, 1) in four independent chains; they
+          // run between the K operand reads and the QK^T, which wait on those
+          // reads anyway (a ones-operand MFMA here cost a fifth of the P·V's
+          // matrix cycles)
+          typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+          typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+          const bf2_t one2 = __builtin_bit_cast(bf2_t, kBf16Ones);
+          float l4[4] = {0.f, 0.f, 0.f, 0.f};
+          static_for<8>([&](auto ST) {
+            // the pairs through a bf16x8 view and shuffles: a bit_cast of a
+            // single dword of the v4i compiled to the wrong dword
+            const bf8_t x = __builtin_bit_cast(bf8_t, Pb[decltype(ST)::value]);
+            l4[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one2, l4[0], false);
+            l4[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one2, l4[1], false);
+            l4[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one2, l4[2], false);
+            l4[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one2, l4[3], false);
+          });
+          Lh += (l4[0] + l4[1]) + (l4[2] + l4[3]);
         }
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -854,7 +872,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int i = 0; i < 16; ++i) S[kb][i] = mask_range(S[kb][i], 32 * kb + i, low, row_span);
     }
     if constexpr (BF)
-      softmax_tile32_bf16<NDB>(S, cexp, m_run, O, L, Pb);
+      softmax_tile32_bf16<NDB>(S, cexp, m_run, O, Lh, Pb);
     else if constexpr (FAST)
       softmax_tile32_single<NDB>(S, cexp, m_run, O, L, Phi, psc, lh);
     else
@@ -878,7 +896,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // side of it.
     if constexpr (decltype(with_pv)::value) {
       static_for<NDB>([&](auto DB) { keep_in_vgprs(O[decltype(DB)::value]); });
-      keep_in_vgprs(L);
+      if constexpr (BF) keep_in_vgprs(Lh); else keep_in_vgprs(L);
     }
     static_for<4>([&](auto KB) { keep_in_vgprs(S[decltype(KB)::value]); });
     // the next tile of the stream must have landed (from this wave) before the
@@ -906,7 +924,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (jn < n_items) load_q(jn, wq);
     mfma_step(nt, std::true_type{}, std::false_type{});
     static_for<NDB>([&](auto DB) { keep_in_vgprs(O[decltype(DB)::value]); });
-    keep_in_vgprs(L);
+    if constexpr (BF) keep_in_vgprs(Lh); else keep_in_vgprs(L);
     phase_barrier();
     store_rows();
     if (jn < n_items) {

@@ -305,6 +305,13 @@ __device__ __forceinline__ float max_with_lane_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Sum over the two lanes l and l^32 (as above; the sum is commutative, so
+// both lanes of a pair get the same bits).
+__device__ __forceinline__ float sum_with_lane_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Maximum over the two lanes l and l^16 (v_permlane16_swap exchanges the
 // odd and even 16-lane rows; as above, the pair holds the partner's value).
 __device__ __forceinline__ float max_with_lane_xor16(float v) {
@@ -584,8 +591,9 @@ __device__ __forceinline__ void softmax_tile32_single(v16f (&S)[4], float c, flo
 // P^T operand of MFMA step st (16 keys): lane (q, h) supplies elements
 // 8*(st%2) .. +7 of key block st/2, i.e. dwords P[st][0..3] hold the bf16
 // pairs of S[st/2][8*(st%2) + 2w], S[st/2][8*(st%2) + 2w + 1].
+// Lh is the lane's share of its row's sum of weights, rescaled with O.
 template <int NO>
-__device__ __forceinline__ void softmax_tile32_bf16(v16f (&S)[4], float c, float& m_run, v16f (&O)[NO], v16f& L,
+__device__ __forceinline__ void softmax_tile32_bf16(v16f (&S)[4], float c, float& m_run, v16f (&O)[NO], float& Lh,
                                                     v4i (&P)[8]) {
   float m4[4];
 #pragma unroll
@@ -606,7 +614,7 @@ __device__ __forceinline__ void softmax_tile32_bf16(v16f (&S)[4], float c, float
     const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
     for (int o = 0; o < NO; ++o) O[o] *= alpha;
-    L *= alpha;
+    Lh *= alpha;
     m_run = m_new;
   }
   const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
