@@ -21,10 +21,13 @@
 //     waves share each 128-key K/V tile staged in LDS.  Per tile and wave:
 //       S^T = K·Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 x FP4),
 //       FP32 online softmax in the log2 domain with lazy rescaling,
-//       P split into two E4M3 terms (hi + residual) with a per-(row, tile)
-//       E8M0 range scale,
-//       O^T += V^T·P^T on the same instruction in FP8 x FP8 (twice: hi, lo),
-//       and the row sums of the quantized weights as 1·P^T.
+//       then by default P rounded to bf16 and O^T += V^T·P^T on
+//       v_mfma_f32_32x32x16_bf16 against V widened exactly to bf16 (the
+//       records then hold bf16 V), the row sums of the bf16 weights by
+//       v_dot2_f32_bf16 on the vector unit; or, in the FP8 formats, P split
+//       into two E4M3 terms (hi + residual) with a per-(row, tile) E8M0
+//       range scale, O^T += V^T·P^T on the scaled FP8 x FP8 instruction
+//       (twice: hi, lo) and the row sums as 1·P^T on the same instruction.
 //     Computing S^T and O^T (instead of S and O) puts one query per lane
 //     column in both, so the softmax state, the P operand and the output rows
 //     need no cross-lane transposes.  The 32x32x64 shape keeps the matrix
@@ -736,7 +739,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
 
 
-  // MFMA step k: O^T += V^T·P^T and L += 1·P^T for tile k-1 (FP8 x FP8),
+  // MFMA step k: O^T += V^T·P^T and the row sums for tile k-1,
   // then S^T = K·Q^T for tile k (FP4 x FP4; both operands' E8M0 scales are
   // applied inside the instruction, so the scores come out dequantized).
   // LDS reads are software-pipelined against the matrix instructions: the V
