@@ -712,8 +712,8 @@ verify_pingpong_kernel(DecodeArgs a) {
     L = mfma16x16x128<kFmtFp8, kFmtFp8>(ones, Plo, L, 127, psc - 4);
   };
 
-  // ---- the ping-pong.  Iteration k of a group: a matrix phase (the lo half
-  // of the two-term split of tile k - 1, the QK^T of tile k, the P·V of tile
+  // ---- the ping-pong.  Iteration k of a group: a matrix phase (the two-term
+  // split of tile k - 1's weights, the QK^T of tile k, the P·V of tile
   // k - 1) and a vector phase (tile k's V scales and tail, the loads of phase
   // k, the mask and softmax of tile k), each ended by a workgroup barrier;
   // group 1 runs one phase behind group 0.  Tile k's K sits in K buffer k % 3
@@ -749,7 +749,7 @@ verify_pingpong_kernel(DecodeArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
     static_for<8>([&](auto) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
     });
     if (k >= 1 && k - 1 < nk) pv_tile(gv + bm1 * VBUF);
     __builtin_amdgcn_s_setprio(0);
@@ -771,7 +771,7 @@ verify_pingpong_kernel(DecodeArgs a) {
     issue_v(gv + bm1 * VBUF, vsr[sl]);        // tile k + 2's V
     if (k < nk) {
       mask_tile(2 * k + grp);
-      softmax_tile_hi<ND>(S, W, a.c, m_run, O, L, Phi, psc);
+      softmax_tile_hi<ND>(S, W, a.c, m_run, O, L, psc);
     }
     keep_in_vgprs(Phi);
     static_for<8>([&](auto TT) { keep_in_vgprs(W[decltype(TT)::value]); });

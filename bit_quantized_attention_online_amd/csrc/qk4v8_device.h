@@ -394,11 +394,11 @@ __device__ __forceinline__ void softmax_tile(v4f (&S)[8], float c, float& m_run,
 }
 
 // softmax_tile in two parts with identical arithmetic, for a schedule that
-// runs the second part elsewhere: (1) the online-softmax step and the hi
-// codes, with the weights p / 2^X left in W; (2) the residuals and lo codes.
+// runs the second part elsewhere: (1) the online-softmax step, with the
+// weights p / 2^X left in W; (2) the hi codes, residuals and lo codes.
 template <int ND>
 __device__ __forceinline__ void softmax_tile_hi(v4f (&S)[8], v4f (&W)[8], float c, float& m_run, v4f (&O)[ND],
-                                                v4f& L, v8i& Phi, int& psc) {
+                                                v4f& L, int& psc) {
   float m4[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) m4[g] = fmaxf(fmaxf(S[2 * g][0], S[2 * g][1]), fmaxf(S[2 * g][2], S[2 * g][3]));
@@ -426,14 +426,14 @@ __device__ __forceinline__ void softmax_tile_hi(v4f (&S)[8], v4f (&W)[8], float 
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) W[t][i] = __builtin_amdgcn_exp2f(fmaf(S[t][i], c, -mX));
+}
+
+__device__ __forceinline__ void softmax_tile_lo(v4f (&W)[8], v8i& Phi, v8i& Plo) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const uint32_t h = e4m3_put2_unscaled<false>((uint32_t)Phi[t], W[t][0], W[t][1]);
     Phi[t] = (int)e4m3_put2_unscaled<true>(h, W[t][2], W[t][3]);
   }
-}
-
-__device__ __forceinline__ void softmax_tile_lo(v4f (&W)[8], const v8i& Phi, v8i& Plo) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const auto b01 = __builtin_amdgcn_cvt_pk_f32_fp8(Phi[t], false);
