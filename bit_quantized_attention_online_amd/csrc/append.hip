@@ -92,10 +92,16 @@ __device__ __forceinline__ void append_k(const AppendParams& p, int64_t id, int6
 
 // Workgroup per (b, h, slot): slot s handles tile floor(len/R) + s.  Rows of
 // the tile in [len, end) are new (from v_new); rows in [tile*R, len) were
-// cached earlier and their bf16 values are in the tail buffer.
-template <int D>
+// cached earlier and their bf16 values are in the tail buffer.  With REG
+// (appends of many rows) the new rows stay in registers between the maximum
+// and the encode (a tile holds at most 256 rows: VPT 16-byte chunks per
+// thread), all requested at once; otherwise (a few rows per tile, where the
+// registers would only lower occupancy) they are read twice, the second time
+// from L2.
+template <int D, bool REG>
 __device__ __forceinline__ void append_v(const AppendParams& p, int64_t wg, int slots, float* red) {
   constexpr int CPR = D / 8;                        // 16-byte chunks per row
+  constexpr int VPT = REG ? 256 * CPR / 256 : 1;    // chunks per thread for the largest tile
   const int slot = (int)(wg % slots);
   const int64_t bh = wg / slots;
   const int b = (int)(bh / p.kv_heads), h = (int)(bh - (int64_t)b * p.kv_heads);
@@ -111,13 +117,26 @@ __device__ __forceinline__ void append_v(const AppendParams& p, int64_t wg, int 
   // absolute maximum of the new rows of this tile
   float amax = 0.0f;
   const int nvec_new = (r1 - first_new) * CPR;
-  for (int vi = threadIdx.x; vi < nvec_new; vi += 256) {
+  auto new_chunk = [&](int vi) -> uint4 {
     const int r = first_new + vi / CPR, cc = vi % CPR;
-    const uint4 w = *reinterpret_cast<const uint4*>(p.v_new + b * p.vs[0] + (int64_t)(r - len) * p.vs[1] +
-                                                    h * p.vs[2] + cc * 8);
+    return *reinterpret_cast<const uint4*>(p.v_new + b * p.vs[0] + (int64_t)(r - len) * p.vs[1] + h * p.vs[2] + cc * 8);
+  };
+  auto absmax8 = [&](const uint4& w) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(ws[k])), fabsf(bf16_hi(ws[k]))));
+  };
+  uint4 wv[VPT];
+  if constexpr (REG) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int vi = (int)threadIdx.x + 256 * i;
+      wv[i] = vi < nvec_new ? new_chunk(vi) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) absmax8(wv[i]);
+  } else {
+    for (int vi = threadIdx.x; vi < nvec_new; vi += 256) absmax8(new_chunk(vi));
   }
   amax = block_max256(amax, red);
   uint8_t* const scale_ptr = p.v_scales + vscale_index(p, b, h, tile);
@@ -139,11 +158,18 @@ __device__ __forceinline__ void append_v(const AppendParams& p, int64_t wg, int 
       *reinterpret_cast<uint2*>(codes + (int64_t)i * D + cc * 8) = e4m3_quantize8(w, inv);
     }
   }
-  for (int vi = threadIdx.x; vi < nvec_new; vi += 256) {
+  auto put_chunk = [&](int vi, const uint4& w) {
     const int r = first_new + vi / CPR, cc = vi % CPR;
-    const uint4 w = *reinterpret_cast<const uint4*>(p.v_new + b * p.vs[0] + (int64_t)(r - len) * p.vs[1] +
-                                                    h * p.vs[2] + cc * 8);
     *reinterpret_cast<uint2*>(codes + (int64_t)(r - r0) * D + cc * 8) = e4m3_quantize8(w, inv);
+  };
+  if constexpr (REG) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int vi = (int)threadIdx.x + 256 * i;
+      if (vi < nvec_new) put_chunk(vi, wv[i]);
+    }
+  } else {
+    for (int vi = threadIdx.x; vi < nvec_new; vi += 256) put_chunk(vi, new_chunk(vi));
   }
   if (threadIdx.x == 0) *scale_ptr = (uint8_t)(X + 127);
   if (slot != 0) return;
@@ -162,11 +188,11 @@ __device__ __forceinline__ void append_v(const AppendParams& p, int64_t wg, int 
   }
 }
 
-template <int D>
+template <int D, bool REG>
 __global__ void __launch_bounds__(256) append_kernel(AppendParams p, int slots, int64_t v_wgs, int64_t total_k) {
   __shared__ float red[4];
   if ((int64_t)blockIdx.x < v_wgs)
-    append_v<D>(p, blockIdx.x, slots, red);
+    append_v<D, REG>(p, blockIdx.x, slots, red);
   else
     append_k<D>(p, ((int64_t)blockIdx.x - v_wgs) * 256 + threadIdx.x, total_k);
 }
@@ -181,8 +207,13 @@ static hipError_t launch_append_d(const AppendParams& p, hipStream_t stream) {
   const int64_t v_wgs = bh * slots;
   const int64_t total_k = bh * p.n_new * (D / 32);
   const int64_t k_wgs = (total_k + 255) / 256;
-  hipLaunchKernelGGL((append_kernel<D>), dim3((unsigned)(v_wgs + k_wgs)), dim3(256), 0, stream, p, slots, v_wgs,
-                     total_k);
+  const dim3 grid((unsigned)(v_wgs + k_wgs));
+  // tiles of many new rows keep them in registers (prompts); a few rows per
+  // sequence (decode steps, drafted blocks) take the low-register variant
+  if (p.n_new >= 64)
+    hipLaunchKernelGGL((append_kernel<D, true>), grid, dim3(256), 0, stream, p, slots, v_wgs, total_k);
+  else
+    hipLaunchKernelGGL((append_kernel<D, false>), grid, dim3(256), 0, stream, p, slots, v_wgs, total_k);
   return hipGetLastError();
 }
 
