@@ -773,7 +773,6 @@ verify_pingpong_kernel(DecodeArgs a) {
       mask_tile(2 * k + grp);
       softmax_tile_hi<ND>(S, W, a.c, m_run, O, L, psc);
     }
-    keep_in_vgprs(Phi);
     static_for<8>([&](auto TT) { keep_in_vgprs(W[decltype(TT)::value]); });
     __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): LDS writes done before the barrier
     phase_barrier();
