@@ -323,3 +323,32 @@ def test_decode_auto_split_count_on_mi355x(gpu):
         forced = ops.decode_workspace_bytes(q, kc, w["kv_len"], w["v_tile_rows"], num_splits=want)
         print(f"[case] auto splits {w['name']}: {auto} vs {forced} bytes", flush=True)
         assert auto == forced > 0
+
+
+@pytest.mark.parametrize("Hq,Hkv,q_len,R,splits", [(8, 2, 1, 256, 1), (64, 8, 8, 64, 0)])
+def test_decode_growing_scores_rescale(gpu, Hq, Hkv, q_len, R, splits):
+    """Decode (one split, one row per query head) and block verify (the
+    64-row ping-pong workgroup) over keys whose scores grow along the cache
+    by several times the lazy-rescale headroom: the running maximum moves
+    during the walk and the accumulators and row sums are rescaled."""
+    from bit_quantized_attention_online_amd import ops
+    B, d, n = 1, 128, 1000
+    rng = np.random.default_rng(Hq + q_len)
+    u = rng.standard_normal(d)
+    q = synth.bf16_bits((u + 0.3 * rng.standard_normal((B, q_len, Hq, d))).astype(np.float32))
+    k = synth.bf16_bits(((np.arange(n) / 600)[None, None, :, None] * u
+                         + 0.3 * rng.standard_normal((B, Hkv, n, d))).astype(np.float32))
+    v = synth.bf16_bits(rng.standard_normal((B, Hkv, n, d)).astype(np.float32))
+    c = math.log2(math.e) / math.sqrt(d)
+    s = synth.bits_to_f32(k[0, 0]).astype(np.float64) @ synth.bits_to_f32(q[0, 0, 0]).astype(np.float64) * c
+    assert s[-128:].max() - s[:128].max() > 16       # the inputs move the maximum far enough
+    print(f"[case] decode growing scores Hq{Hq} Hkv{Hkv} q_len{q_len} R{R} s{splits}", flush=True)
+    kc, ks, vc, vs = _cache_from(k, v, R)
+    o, l = ops.attn_decode(to_dev(q), kc, ks, vc, vs, n, v_tile_rows=R, num_splits=splits, return_lse=True)
+    torch.cuda.synchronize()
+    rkc, rks = quant.quantize_qk(k)
+    rvc, rvs = quant.quantize_v(v.reshape(B * Hkv, n, d), R)
+    ro, rl = oatt.qk4v8_decode(q, rkc, rks, rvc.reshape(B, Hkv, n, d), rvs.reshape(B, Hkv, -1),
+                               np.full(B, n, dtype=np.int32), R, 1 / math.sqrt(d))
+    assert_attn_close(from_dev_bf16(o), ro, "decode growing scores")
+    assert np.abs(l.cpu().numpy() - rl).max() < 5e-3

@@ -261,3 +261,33 @@ def test_prefill_hadamard_outlier_channels(gpu):
     for had in (False, True):
         rel = np.linalg.norm(outs[had] - exact) / np.linalg.norm(exact)
         print(f"[report] {'rotated' if had else 'plain'} QK4V8 vs unquantized attention: rel_l2={rel:.3e}", flush=True)
+
+
+def _ramped(B, Hq, Hkv, Nq, Nk, d, seed, slope):
+    """Q rows near one direction u and K rows along u with a weight growing
+    with the key position, so the score of a row grows along the keys."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(d)
+    q = u + 0.3 * rng.standard_normal((B, Hq, Nq, d))
+    k = (np.arange(Nk) * slope)[None, None, :, None] * u + 0.3 * rng.standard_normal((B, Hkv, Nk, d))
+    v = rng.standard_normal((B, Hkv, Nk, d))
+    return tuple(synth.bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("p_mode", P_MODES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_growing_scores_rescale(gpu, causal, p_mode):
+    """Row maxima that grow by several times the lazy-rescale headroom along
+    the keys, so the accumulators and the row sums are rescaled during the
+    walk (the online-softmax correction step)."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 640, 128
+    q, k, v = _ramped(B, Hq, Hkv, N, N, d, seed=21, slope=1 / 400)
+    # the inputs do what the test needs: over the keys the log2-domain score
+    # of a row grows by much more than the 8 units of headroom
+    c = math.log2(math.e) / math.sqrt(d)
+    s = np.einsum("hd,hkd->hk", synth.bits_to_f32(q[0, 0::Hq // Hkv, -1]).astype(np.float64),
+                  synth.bits_to_f32(k[0]).astype(np.float64)) * c
+    assert (s[:, -128:].max(axis=1) - s[:, :128].max(axis=1)).min() > 12
+    o, l, ro, rl = _run(q, k, v, causal, 64, p_mode=p_mode)
+    assert_attn_close(o, ro, f"growing scores causal={causal} p_mode={p_mode}")
+    assert np.abs(l - rl).max() < 5e-3
