@@ -291,3 +291,36 @@ def test_prefill_growing_scores_rescale(gpu, causal, p_mode):
     o, l, ro, rl = _run(q, k, v, causal, 64, p_mode=p_mode)
     assert_attn_close(o, ro, f"growing scores causal={causal} p_mode={p_mode}")
     assert np.abs(l - rl).max() < 5e-3
+
+
+@pytest.mark.parametrize("p_mode", P_MODES)
+@pytest.mark.parametrize("case", ["zero_q", "zero_k", "const_v", "zero_v"])
+def test_prefill_degenerate_inputs(gpu, case, p_mode):
+    """Degenerate inputs of the method: all-zero Q or K blocks (E8M0 floor,
+    every score 0, uniform weights over the visible keys), a constant V
+    (every row of the output is that value) and an all-zero V."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 300, 128
+    q, k, v = _inputs(B, Hq, Hkv, N, N, d, seed=31)
+    if case == "zero_q":
+        q[:] = 0
+    elif case == "zero_k":
+        k[:] = 0
+    elif case == "const_v":
+        v[:] = synth.bf16_bits(np.full(1, 1.375, np.float32))[0]
+    else:
+        v[:] = 0
+    o, l, ro, rl = _run(q, k, v, True, 64, p_mode=p_mode)
+    assert_attn_close(o, ro, f"degenerate {case} p_mode={p_mode}")
+    assert np.abs(l - rl).max() < 5e-3
+    if case == "const_v":
+        # 1.375 is exact in E4M3 (times the tile's power of two) and in bf16,
+        # and the output divides the weighted sum by the sum of the same
+        # weights: every output element is 1.375 after the bf16 rounding
+        assert (o == 1.375).all()
+    if case == "zero_v":
+        assert not o.any()
+    if case in ("zero_q", "zero_k"):
+        # every score 0, so every weight is exactly 1 (bf16, or hi = 2^7 and
+        # lo = 0 in the two-term split): row i is the mean of the visible
+        # rows of V-hat, up to the fp32 sums and the bf16 rounding
+        assert (np.abs(o - ro) <= np.abs(ro) * 2.0 ** -8 + 1e-4).all()
