@@ -352,3 +352,36 @@ def test_decode_growing_scores_rescale(gpu, Hq, Hkv, q_len, R, splits):
                                np.full(B, n, dtype=np.int32), R, 1 / math.sqrt(d))
     assert_attn_close(from_dev_bf16(o), ro, "decode growing scores")
     assert np.abs(l.cpu().numpy() - rl).max() < 5e-3
+
+
+@pytest.mark.parametrize("Hq,Hkv,q_len,R", [(8, 2, 1, 256), (64, 8, 8, 64)])
+@pytest.mark.parametrize("case", ["zero_q", "const_v"])
+def test_decode_degenerate_inputs(gpu, Hq, Hkv, q_len, R, case):
+    """All-zero queries (exact uniform weights over the visible keys) and a
+    constant V cache (every output element is that value), for decode and
+    for the 64-row block-verify workgroup."""
+    from bit_quantized_attention_online_amd import ops
+    B, d, n = 2, 128, 700
+    rng = np.random.default_rng(q_len + 3)
+    q = synth.bf16_bits(rng.standard_normal((B, q_len, Hq, d)).astype(np.float32))
+    k = synth.bf16_bits(rng.standard_normal((B, Hkv, n, d)).astype(np.float32))
+    v = synth.bf16_bits(rng.standard_normal((B, Hkv, n, d)).astype(np.float32))
+    if case == "zero_q":
+        q[:] = 0
+    else:
+        v[:] = synth.bf16_bits(np.full(1, -0.8125, np.float32))[0]
+    print(f"[case] decode degenerate {case} Hq{Hq} q_len{q_len} R{R}", flush=True)
+    kc, ks, vc, vs = _cache_from(k, v, R)
+    o, l = ops.attn_decode(to_dev(q), kc, ks, vc, vs, n, v_tile_rows=R, return_lse=True)
+    torch.cuda.synchronize()
+    o = from_dev_bf16(o)
+    rkc, rks = quant.quantize_qk(k)
+    rvc, rvs = quant.quantize_v(v.reshape(B * Hkv, n, d), R)
+    ro, rl = oatt.qk4v8_decode(q, rkc, rks, rvc.reshape(B, Hkv, n, d), rvs.reshape(B, Hkv, -1),
+                               np.full(B, n, dtype=np.int32), R, 1 / math.sqrt(d))
+    assert_attn_close(o, ro, f"decode degenerate {case}")
+    assert np.abs(l.cpu().numpy() - rl).max() < 5e-3
+    if case == "const_v":
+        assert (o == -0.8125).all()      # exact in E4M3 (times the tile's power of two) and in bf16
+    else:
+        assert (np.abs(o - ro) <= np.abs(ro) * 2.0 ** -8 + 1e-4).all()
