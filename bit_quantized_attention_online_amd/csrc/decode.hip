@@ -489,20 +489,21 @@ __device__ __forceinline__ v2i lds_read_tr8(const uint8_t* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)p);
 }
 
-// One 16-byte (or 4-byte) piece per lane from global memory straight into
-// LDS, through a buffer resource (a load with the LDS bit): lane l copies
-// bytes voffset .. voffset + SIZE - 1 of the resource's range to lds_base +
-// SIZE * l (lds_base wave-uniform).  Lanes past the range read nothing from
-// memory.  Completion is counted in vmcnt like any other load.
+// One 16-byte piece per lane from global memory straight into LDS, through
+// a buffer resource (a load with the LDS bit): lane l copies bytes voffset ..
+// voffset + 15 of the resource's range to lds_base + 16 l (lds_base
+// wave-uniform).  Lanes past the range read nothing from memory.  Completion
+// is counted in vmcnt like any other load.  The 1-byte form writes the byte
+// zero-extended to the dword at lds_base + 4 l.
 __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint8_t* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_base)), 16,
       voffset, 0, 0, kNT);
 }
-__device__ __forceinline__ void load_to_lds4(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint8_t* lds_base) {
+__device__ __forceinline__ void load_to_lds1(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint8_t* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_base)), 4,
-      voffset, 0, 0, kNT);
+      r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_base)), 1,
+      voffset, 0, 0, 0);
 }
 
 // vmcnt(N) on gfx9: vm_cnt[3:0] | exp_cnt[6:4] | lgkm_cnt[11:8] | vm_cnt[5:4]
@@ -526,10 +527,9 @@ verify_pingpong_kernel(DecodeArgs a) {
   using T = DecTile<D>;
   constexpr int NB = T::NB, ND = D / 16;
   static_assert(NB == 4 && D == 128, "one dword of K scales per key; 1 KB holds 16 K rows or 8 V rows");
-  constexpr int KBUF = T::K + 1024;   // K codes, then the scales (wave w's 32 keys at 256 w)
-  constexpr int VBUF = T::V + 16;     // V codes, then the four 32-key scales
+  constexpr int KBUF = T::K + 1024;   // K codes, then the scales (key j's dword at 4 j)
+  constexpr int VBUF = T::V + 256;    // V codes, then the 32-key scales (group g's byte at 4 g)
   constexpr int GRP = 3 * KBUF + 3 * VBUF;
-  constexpr int kPhaseLoads = 8;      // loads one wave issues per vector phase
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * GRP];
 
   // the wave index through readfirstlane: known wave-uniform, so the load
@@ -537,6 +537,9 @@ verify_pingpong_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;          // group 0 runs one phase ahead of group 1
   const int rb = wave & 3;            // this wave's 16-row block
+  // loads one wave issues per vector phase: the K and V codes (2 + 4), and
+  // the tile's K scales (wave 0) or its V scales (wave 1)
+  const int phase_loads = rb < 2 ? 7 : 6;
   uint8_t* gk = lds + grp * GRP;      // K buffer i at gk + i * KBUF
   uint8_t* gv = gk + 3 * KBUF;        // V buffer i at gv + i * VBUF
   const int ql = lane & 15, lg = lane >> 4;
@@ -606,8 +609,11 @@ verify_pingpong_kernel(DecodeArgs a) {
   Cursor kcur = cursor_at(j_begin + grp * 128), vcur = kcur;
   // K codes: wave rb fills LDS kilobytes 2 rb and 2 rb + 1 (16 rows each);
   // the lane writing LDS chunk position p of row r fetches chunk p ^ ((r /
-  // 16) % 4), the K-row swizzle.  K scales: lanes 0..31 of wave rb fetch the
-  // dwords of keys 32 rb .. 32 rb + 31; lanes 32..63 point past the range.
+  // 16) % 4), the K-row swizzle.  K scales: wave 0 alone, 16 bytes (four
+  // keys) per lane, lanes 32..63 past the range (they write zeros to the
+  // second half of the 1 KB scale area); one load instead of one per wave,
+  // since every load instruction costs the issuing SIMD time whatever its
+  // size.
   auto issue_k = [&](uint8_t* kb) __attribute__((always_inline)) {
     int rows;
     int64_t row, vs0;
@@ -620,14 +626,15 @@ verify_pingpong_kernel(DecodeArgs a) {
       const int c = rb * 2 + decltype(I)::value;
       load_to_lds16(rk, (uint32_t)(c * 1024 + (lane >> 2) * 64 + (((lane & 3) ^ (c & 3)) * 16)), kb + c * 1024);
     });
-    load_to_lds4(rs, lane < 32 ? (uint32_t)((rb * 32 + lane) * 4) : 1024u, kb + T::K + rb * 256);
+    if (rb == 0) load_to_lds16(rs, (uint32_t)(lane * 16), kb + T::K);
     advance(kcur);
   };
   // V codes: wave rb fills LDS kilobytes 4 rb .. 4 rb + 3 (8 rows each);
   // the lane writing chunk position p of row r fetches chunk p ^ (r % 8).
-  // The V scale of 32-key group lane % 4 comes into a register first (a
-  // group past the sequence takes the last row's scale).
-  auto issue_v = [&](uint8_t* vb, uint8_t& vsreg) __attribute__((always_inline)) {
+  // V scales: wave 1 alone, lane l the byte of 32-key group l % 4 (a group
+  // past the sequence takes the last row's scale) into LDS dword l,
+  // zero-extended, so dword g holds group g's scale.
+  auto issue_v = [&](uint8_t* vb) __attribute__((always_inline)) {
     int rows;
     int64_t row, vs0;
     locate(vcur, rows, row, vs0);
@@ -636,7 +643,7 @@ verify_pingpong_kernel(DecodeArgs a) {
     const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.vsc + vs0 + (vcur.slot >> a.log2R)), (short)0, rows > 0 ? 8 : 0, 0x00020000);
     const int vrow = (vcur.slot & ((1 << a.log2R) - 1)) + min(32 * (lane & 3), max(rows, 1) - 1);
-    vsreg = __builtin_amdgcn_raw_buffer_load_b8(rvs, vrow >> a.log2R, 0, 0);
+    if (rb == 1) load_to_lds1(rvs, (uint32_t)(vrow >> a.log2R), vb + T::V);
     static_for<4>([&](auto I) {
       const int c = rb * 4 + decltype(I)::value;
       load_to_lds16(rv, (uint32_t)(c * 1024 + (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) * 16)), vb + c * 1024);
@@ -667,7 +674,7 @@ verify_pingpong_kernel(DecodeArgs a) {
       const int key = subtile_key(t, ql);
       const v4i kv = *reinterpret_cast<const v4i*>(kb + key * T::KRB + kchunk);
       const v8i af = fp4_operand(make_uint4((uint32_t)kv[0], (uint32_t)kv[1], (uint32_t)kv[2], (uint32_t)kv[3]));
-      const int sa = (int)((ks[(key >> 5) * 64 + (key & 31)] >> (8 * lg)) & 0xFF);
+      const int sa = (int)((ks[key] >> (8 * lg)) & 0xFF);
       S[t] = mfma16x16x128<kFmtFp4, kFmtFp4>(af, qf, v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc);
     }
   };
@@ -686,7 +693,7 @@ verify_pingpong_kernel(DecodeArgs a) {
   // accumulate into the same registers, so an independent instruction
   // between them keeps a wave alone on its SIMD from stalling
   auto pv_tile = [&](const uint8_t* vb) __attribute__((always_inline)) {
-    const int vs = vb[T::V + lg];
+    const int vs = reinterpret_cast<const uint32_t*>(vb + T::V)[lg];
     const int src_row_in_piece = ql >> 1, src_half = ql & 1;
     auto v_operand = [&](int dd) __attribute__((always_inline)) {
       v8i av;
@@ -721,23 +728,20 @@ verify_pingpong_kernel(DecodeArgs a) {
   // phase's QK^T has run, the V buffer of tile k - 1 once its P·V has. ----
   const int nk = (ntiles - grp + 1) / 2;      // this group's tiles
   const int n_it = (ntiles + 1) / 2;          // group 0's: both groups run n_it + 1 iterations, rounded up to pairs
-  uint8_t vsr[2];                             // V scales of the tiles requested two phases back
   issue_k(gk);                                // tile 0's K
   issue_k(gk + KBUF);                         // "phase -2": tile 1's K, tile 0's V
-  issue_v(gv, vsr[0]);
+  issue_v(gv);
   issue_k(gk + 2 * KBUF);                     // "phase -1": tile 2's K, tile 1's V
-  issue_v(gv + VBUF, vsr[1]);
-  wait_loads<2 * kPhaseLoads>();              // this wave's part of tile 0's K has landed
+  issue_v(gv + VBUF);
+  // this wave's part of tile 0's K has landed
+  if (phase_loads == 7) wait_loads<14>(); else wait_loads<12>();
   phase_barrier();
   if (grp == 1) phase_barrier();
   v4f W[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) W[t] = v4f{0.f, 0.f, 0.f, 0.f};
   int b3 = 0;                                 // k % 3
-  constexpr std::integral_constant<int, 0> I0{};
-  constexpr std::integral_constant<int, 1> I1{};
-  auto iteration = [&](int k, auto SL) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SL)::value;   // k % 2
+  auto iteration = [&](int k) __attribute__((always_inline)) {
     const int bm1 = b3 == 0 ? 2 : b3 - 1;     // (k - 1) % 3, also (k + 2) % 3
     __builtin_amdgcn_s_setprio(1);
     // unconditional (their results are used only when the P·V and the
@@ -761,14 +765,12 @@ verify_pingpong_kernel(DecodeArgs a) {
     phase_barrier();
     // the loads of phase k - 2 have landed: tile k's V (read by the next
     // P·V) and tile k + 1's K (the next QK^T)
-    wait_loads<kPhaseLoads>();
-    uint8_t* vk = gv + b3 * VBUF;
-    vk[T::V + (lane & 3)] = vsr[sl];
-    if (k < nk) clear_tail(vk, 2 * k + grp);
+    if (phase_loads == 7) wait_loads<7>(); else wait_loads<6>();
+    if (k < nk) clear_tail(gv + b3 * VBUF, 2 * k + grp);
     // the next loads before the softmax (measured: 2-3% faster than after it,
     // where the waves of a group wait for the memory pipeline at the barrier)
     issue_k(gk + b3 * KBUF);                  // tile k + 3's K
-    issue_v(gv + bm1 * VBUF, vsr[sl]);        // tile k + 2's V
+    issue_v(gv + bm1 * VBUF);                 // tile k + 2's V
     if (k < nk) {
       mask_tile(2 * k + grp);
       softmax_tile_hi<ND>(S, W, a.c, m_run, O, L, psc);
@@ -778,13 +780,12 @@ verify_pingpong_kernel(DecodeArgs a) {
     phase_barrier();
     b3 = b3 == 2 ? 0 : b3 + 1;
   };
-  // unrolled by two (the V-scale register of phase k is vsr[k % 2]), always
-  // whole pairs (an iteration past n_it does nothing but its barriers and
+  // unrolled by two, always whole pairs (an iteration past n_it does nothing but its barriers and
   // empty loads), so the compiler knows at the back edge which loads are in
   // flight
   for (int k = 0; k <= n_it; k += 2) {
-    iteration(k, I0);
-    iteration(k + 1, I1);
+    iteration(k);
+    iteration(k + 1);
   }
   wait_loads<0>();                            // the empty loads past the range still write LDS
   if (grp == 0) phase_barrier();              // matches group 1's initial wait
