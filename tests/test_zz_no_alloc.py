@@ -64,3 +64,34 @@ def test_noalloc_rejects_partials_beyond_the_array(gpu):
     with pytest.raises(ops.QK4V8Error) as e:
         ops.attn_decode_noalloc(q, kc, ks, vc, vs, kv_len, torch.empty_like(q), num_splits=16)
     assert e.value.status == 5
+
+
+@pytest.mark.parametrize("shape", [(8, 64, 8, 1, 4096, 128, 256),    # decode: 2 splits, partials and the merge
+                                   (4, 64, 8, 8, 3000, 128, 256)])   # block verify: one split, direct output
+def test_noalloc_decode_replays_under_graph_capture(gpu, shape):
+    """The allocation-free call captured into a HIP graph, as a serving loop
+    that cannot allocate would run it: every replay, with eager work and a
+    synchronization before each, writes the eager call's bits."""
+    from bit_quantized_attention_online_amd import ops
+    B, Hq, Hkv, q_len, kv_len, d, R = shape
+    print(f"[case] noalloc graph capture B{B} Hq{Hq} Hkv{Hkv} q_len{q_len} kv_len{kv_len}", flush=True)
+    q, kc, ks, vc, vs, lens = _case(B, Hq, Hkv, q_len, kv_len, d, R, seed=300 + q_len)
+    kw = dict(v_tile_rows=R, kv_lens=lens, softmax_scale=1 / math.sqrt(d))
+    ref = torch.empty_like(q)
+    ops.attn_decode_noalloc(q, kc, ks, vc, vs, kv_len, ref, **kw)
+    out = torch.full_like(q, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops.attn_decode_noalloc(q, kc, ks, vc, vs, kv_len, out, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ops.attn_decode_noalloc(q, kc, ks, vc, vs, kv_len, out, **kw)
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
