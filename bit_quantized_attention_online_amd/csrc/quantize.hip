@@ -11,22 +11,6 @@
 
 namespace qk4v8 {
 
-namespace {
-
-// The quantizers stream their input once and write codes that the attention
-// kernels read later: both sides go through the non-temporal path (loads
-// and stores with the nt bit), which keeps the stream from displacing
-// cached lines.
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint4 load_nt16(const uint16_t* p) {
-  const v4u r = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-  return make_uint4(r[0], r[1], r[2], r[3]);
-}
-
-}  // namespace
-
 // One lane per 8 consecutive elements; 4 adjacent lanes own one 32-element
 // block and combine their maxima with two xor-shuffles.  Loads are 16 B per
 // lane and the code stores 4 B per lane, both contiguous across the wave.
@@ -86,7 +70,7 @@ __global__ void __launch_bounds__(256) quantize_qk_kernel(const uint16_t* __rest
       for (int k = 0; k < 4; ++k) c |= e2m1_pack2(bf16_lo(ws[k]) * inv, bf16_hi(ws[k]) * inv) << (8 * k);
     }
     if (live) {
-      __builtin_nontemporal_store(c, reinterpret_cast<uint32_t*>(codes + row * (d >> 1) + chunk * 4));
+      store_nt4(codes + row * (d >> 1) + chunk * 4, c);
       if ((chunk & 3) == 0) scales[row * (d >> 5) + (chunk >> 2)] = (uint8_t)(X + 127);
     }
   }
@@ -128,10 +112,7 @@ __global__ void __launch_bounds__(256) quantize_v_kernel(const uint16_t* __restr
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int vi = threadIdx.x + i * 256;
-    if (vi < nvec) {
-      const uint2 c = e4m3_quantize8(w[i], inv);
-      __builtin_nontemporal_store(v2u{c.x, c.y}, reinterpret_cast<v2u*>(dst + (int64_t)vi * 8));
-    }
+    if (vi < nvec) store_nt8(dst + (int64_t)vi * 8, e4m3_quantize8(w[i], inv));
   }
   if (threadIdx.x == 0) scales[g * n_tiles + t] = (uint8_t)(X + 127);
 }
