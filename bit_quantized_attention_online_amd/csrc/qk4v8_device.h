@@ -660,10 +660,10 @@ __device__ __forceinline__ uint2 e4m3_quantize8(uint4 w, float inv) {
 // Streaming access for the quantizers: loads of inputs read once and stores
 // of codes that another kernel reads later carry the non-temporal bit, so
 // the stream does not displace cached lines (the V quantizer: 9.6 -> 7.7 us
-// for 50 MB).  Each wave's stores there cover whole 128-byte lines; the KV
-// append, whose K-code rows are 64-byte pieces spread over the cache, ran
-// slower with it (16.9 -> 22.4 us for a 4096-token prompt) and keeps plain
-// accesses.
+// for 50 MB), where each wave's stores cover whole 128-byte lines.  The KV
+// append ran slower with the hint on its loads and code stores (16.9 ->
+// 22.4 us for a 4096-token prompt; its K-code rows are 64-byte pieces spread
+// over the cache, its inputs token-major rows) and keeps plain accesses.
 typedef uint32_t v4u_nt __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u_nt __attribute__((ext_vector_type(2)));
 
