@@ -232,3 +232,45 @@ def _append(**kw):
 ])
 def test_append_validation(kw, status):
     assert ops.lib().qk4v8_kv_append(ctypes.byref(_append(**kw)), None) == status
+
+
+C_CALLER = r'''
+#include "qk4v8.h"
+#include <stdio.h>
+#include <string.h>
+int main(void) {
+  uint16_t x[32] = {0};
+  uint8_t codes[16], scales[1];
+  qk4v8_decode_args d;
+  memset(&d, 0, sizeof d);
+  if (qk4v8_abi_version() != QK4V8_ABI_VERSION) return 1;
+  if (qk4v8_status_string(QK4V8_ERR_SHAPE) == NULL) return 2;
+  if (qk4v8_quantize_qk(x, -1, 32, 32, codes, scales, NULL) != QK4V8_ERR_SHAPE) return 3;
+  if (qk4v8_quantize_qk(x, 0, 32, 32, codes, scales, NULL) != QK4V8_OK) return 4;
+  if (qk4v8_attn_decode(NULL, NULL) != QK4V8_ERR_NULL) return 5;
+  if (qk4v8_attn_decode(&d, NULL) != QK4V8_ERR_SHAPE) return 6;
+  printf("abi %d\n", qk4v8_abi_version());
+  return 0;
+}
+'''
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """The boundary is a C ABI: a C99 program (gcc, no C++) includes the
+    header, links the library and gets the documented statuses back from
+    calls that fail validation before any GPU work."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    lib_dir = os.path.dirname(ops._LIB_PATH)
+    if not os.path.exists(ops._LIB_PATH):
+        pytest.skip("libqk4v8.so not built")
+    src, exe = tmp_path / "caller.c", tmp_path / "caller"
+    src.write_text(C_CALLER)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe), "-L", lib_dir, "-lqk4v8",
+                    "-Wl,-rpath," + lib_dir], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.strip() == f"abi {ops.lib().qk4v8_abi_version()}"
