@@ -493,11 +493,17 @@ __device__ __forceinline__ v2i lds_read_tr8(const uint8_t* __restrict__ p) {
 // a buffer resource (a load with the LDS bit): lane l copies bytes voffset ..
 // voffset + 15 of the resource's range to lds_base + 16 l (lds_base
 // wave-uniform).  Lanes past the range read nothing from memory.  Completion
-// is counted in vmcnt like any other load.  The 1-byte form writes the byte
+// is counted in vmcnt like any other load.  The 4-byte form copies bytes
+// voffset .. voffset + 3 to lds_base + 4 l; the 1-byte form writes the byte
 // zero-extended to the dword at lds_base + 4 l.
 __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint8_t* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_base)), 16,
+      voffset, 0, 0, kNT);
+}
+__device__ __forceinline__ void load_to_lds4(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_base)), 4,
       voffset, 0, 0, kNT);
 }
 __device__ __forceinline__ void load_to_lds1(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint8_t* lds_base) {
@@ -527,7 +533,7 @@ verify_pingpong_kernel(DecodeArgs a) {
   using T = DecTile<D>;
   constexpr int NB = T::NB, ND = D / 16;
   static_assert(NB == 4 && D == 128, "one dword of K scales per key; 1 KB holds 16 K rows or 8 V rows");
-  constexpr int KBUF = T::K + 1024;   // K codes, then the scales (key j's dword at 4 j)
+  constexpr int KBUF = T::K + 1024;   // K codes, then the scales (in read order, scale_slot)
   constexpr int VBUF = T::V + 256;    // V codes, then the 32-key scales (group g's byte at 4 g)
   constexpr int GRP = 3 * KBUF + 3 * VBUF;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * GRP];
@@ -538,8 +544,8 @@ verify_pingpong_kernel(DecodeArgs a) {
   const int grp = wave >> 2;          // group 0 runs one phase ahead of group 1
   const int rb = wave & 3;            // this wave's 16-row block
   // loads one wave issues per vector phase: the K and V codes (2 + 4), and
-  // the tile's K scales (wave 0) or its V scales (wave 1)
-  const int phase_loads = rb < 2 ? 7 : 6;
+  // half of the tile's K scales (waves 0 and 2) or its V scales (wave 1)
+  const int phase_loads = rb < 3 ? 7 : 6;
   uint8_t* gk = lds + grp * GRP;      // K buffer i at gk + i * KBUF
   uint8_t* gv = gk + 3 * KBUF;        // V buffer i at gv + i * VBUF
   const int ql = lane & 15, lg = lane >> 4;
@@ -609,11 +615,11 @@ verify_pingpong_kernel(DecodeArgs a) {
   Cursor kcur = cursor_at(j_begin + grp * 128), vcur = kcur;
   // K codes: wave rb fills LDS kilobytes 2 rb and 2 rb + 1 (16 rows each);
   // the lane writing LDS chunk position p of row r fetches chunk p ^ ((r /
-  // 16) % 4), the K-row swizzle.  K scales: wave 0 alone, 16 bytes (four
-  // keys) per lane, lanes 32..63 past the range (they write zeros to the
-  // second half of the 1 KB scale area); one load instead of one per wave,
-  // since every load instruction costs the issuing SIMD time whatever its
-  // size.
+  // 16) % 4), the K-row swizzle.  K scales: waves 0 and 2, one dword per
+  // lane, in the order the QK^T reads them (dword 8 q + t is the scale of
+  // key subtile_key(t, q), so a lane reads its eight as two 16-byte
+  // pieces); two waves rather than one or four, since every load
+  // instruction costs the issuing SIMD time whatever its size.
   auto issue_k = [&](uint8_t* kb) __attribute__((always_inline)) {
     int rows;
     int64_t row, vs0;
@@ -626,7 +632,10 @@ verify_pingpong_kernel(DecodeArgs a) {
       const int c = rb * 2 + decltype(I)::value;
       load_to_lds16(rk, (uint32_t)(c * 1024 + (lane >> 2) * 64 + (((lane & 3) ^ (c & 3)) * 16)), kb + c * 1024);
     });
-    if (rb == 0) load_to_lds16(rs, (uint32_t)(lane * 16), kb + T::K);
+    if ((rb & 1) == 0) {
+      const int slot = (rb >> 1) * 64 + lane;
+      load_to_lds4(rs, (uint32_t)(subtile_key(slot & 7, slot >> 3) * 4), kb + T::K + (rb >> 1) * 256);
+    }
     advance(kcur);
   };
   // V codes: wave rb fills LDS kilobytes 4 rb .. 4 rb + 3 (8 rows each);
@@ -668,13 +677,14 @@ verify_pingpong_kernel(DecodeArgs a) {
   v4f S[8];
   int psc = 127;
   auto qk_tile = [&](const uint8_t* kb) __attribute__((always_inline)) {
-    const uint32_t* ks = reinterpret_cast<const uint32_t*>(kb + T::K);
+    const v4i* ks = reinterpret_cast<const v4i*>(kb + T::K + ql * 32);
+    const v4i ks0 = ks[0], ks1 = ks[1];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int key = subtile_key(t, ql);
       const v4i kv = *reinterpret_cast<const v4i*>(kb + key * T::KRB + kchunk);
       const v8i af = fp4_operand(make_uint4((uint32_t)kv[0], (uint32_t)kv[1], (uint32_t)kv[2], (uint32_t)kv[3]));
-      const int sa = (int)((ks[key] >> (8 * lg)) & 0xFF);
+      const int sa = (int)(((uint32_t)(t < 4 ? ks0[t & 3] : ks1[t & 3]) >> (8 * lg)) & 0xFF);
       S[t] = mfma16x16x128<kFmtFp4, kFmtFp4>(af, qf, v4f{0.f, 0.f, 0.f, 0.f}, sa, qsc);
     }
   };
@@ -734,7 +744,7 @@ verify_pingpong_kernel(DecodeArgs a) {
   issue_k(gk + 2 * KBUF);                     // "phase -1": tile 2's K, tile 1's V
   issue_v(gv + VBUF);
   // this wave's part of tile 0's K has landed
-  if (phase_loads == 7) wait_loads<14>(); else wait_loads<12>();
+  if (phase_loads == 7) wait_loads<14>(); else wait_loads<12>();   // after tile 0's K
   phase_barrier();
   if (grp == 1) phase_barrier();
   v4f W[8];
