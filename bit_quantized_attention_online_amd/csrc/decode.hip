@@ -533,7 +533,7 @@ verify_pingpong_kernel(DecodeArgs a) {
   using T = DecTile<D>;
   constexpr int NB = T::NB, ND = D / 16;
   static_assert(NB == 4 && D == 128, "one dword of K scales per key; 1 KB holds 16 K rows or 8 V rows");
-  constexpr int KBUF = T::K + 1024;   // K codes, then the scales (in read order, scale_slot)
+  constexpr int KBUF = T::K + 1024;   // K codes, then the scales (in the order the QK^T reads them)
   constexpr int VBUF = T::V + 256;    // V codes, then the 32-key scales (group g's byte at 4 g)
   constexpr int GRP = 3 * KBUF + 3 * VBUF;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * GRP];
